@@ -1,0 +1,159 @@
+/*
+ * w4a8.h -- C ABI of the MI355X (gfx950) W4A8 codebook linear layer library (libw4a8.so).
+ *
+ * The layer is the asym_w4a8_int8 ("ConvRot") quantised linear described by the model
+ * cards "Qwen3.8-27B-uncensored-w4a8-convrot-ComfyUI" (sections "Format", "Why this
+ * exists", "Reproducing") and "Qwen3.8-27B-W4A8 (for ComfyUI)" (section "Model
+ * Overview").  One quantised layer of N output rows and K input features is four tensors:
+ *
+ *   packed     int8   [N][K/2]   4-bit codebook indices, two per byte; element 2j of a row
+ *                                sits in the low nibble of byte j, element 2j+1 in the high
+ *   s_rel      uint8  [N][K/16]  group scales, OCP fp8 E4M3FN bit patterns, one per 16 values
+ *   s_channel  fp32   [N]        per-output-row scale
+ *   codebook   fp32   [16]       the tensor's 16 levels (a Lloyd-Max fit; any 16 values work)
+ *
+ * and the layer computes, with activations rotated and quantised per token,
+ *
+ *   y[m][r] = s_x[m] * sum_k x_q[m][k] * s_channel[r] * dec(s_rel[r][k/16]) * codebook[idx[r][k]]
+ *
+ * where the rotation is the orthonormal Sylvester Hadamard transform of order 256 applied
+ * to every 256-block of the K axis of both weights (offline) and activations (per call).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, row-major and
+ *    contiguous, owned by the caller, and at least 16-byte aligned.  The library keeps no
+ *    reference to them after the call returns and allocates no device memory.
+ *  - `stream` is a hipStream_t (0 = the null stream).  Work is enqueued asynchronously
+ *    on it; the call returns as soon as the work is enqueued.
+ *  - Arguments are validated before anything is enqueued: on a non-zero status nothing
+ *    was launched and no output was touched.  Faults inside kernels are asynchronous and
+ *    surface at the caller's next synchronisation on the stream.
+ *  - Non-finite inputs are outside the contract (no fault; unspecified output).
+ *  - Calls on distinct streams may run concurrently; calls are re-entrant and thread-safe.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define W4A8_API __attribute__((visibility("default")))
+#else
+#define W4A8_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_ERR_NULL = 1,       /* a required pointer is NULL */
+    W4A8_ERR_SHAPE = 2,      /* M, N or K out of range; K not a multiple of 256 */
+    W4A8_ERR_DTYPE = 3,      /* unknown dtype or algorithm code */
+    W4A8_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
+    W4A8_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required */
+    W4A8_ERR_HIP = 6,        /* a HIP runtime call or kernel launch failed */
+    W4A8_ERR_DEVICE = 7      /* the current device is not a gfx950 (MI355X-class) GPU */
+} w4a8_status;
+
+/* Element types of floating-point inputs and outputs. */
+typedef enum { W4A8_F32 = 0, W4A8_BF16 = 1 } w4a8_dtype;
+
+/* Kernel choice for w4a8_linear_algo. */
+typedef enum {
+    W4A8_ALGO_AUTO = 0,     /* pick by M, N, K (what w4a8_linear does) */
+    W4A8_ALGO_GEMV = 1,     /* fp32-codebook streaming GEMV (decode); M <= 4 and M*K <= 40960 */
+    W4A8_ALGO_MFMA_I8 = 2,  /* int8 MFMA on the int8 form of the codebook, exact int32
+                               per-16 partials, fp32 group-scale fold */
+    W4A8_ALGO_MFMA_F16 = 3  /* f16 MFMA on decoded weights (codebook x group scale in f16) */
+} w4a8_algo;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+W4A8_API int w4a8_version(void);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+W4A8_API const char *w4a8_status_string(int status);
+
+/*
+ * Bytes of device workspace w4a8_quantize_weight needs for an N x K weight
+ * (0 if the shape is invalid).
+ */
+W4A8_API size_t w4a8_quantize_weight_workspace(int64_t N, int64_t K);
+
+/*
+ * Offline quantisation of one weight matrix into the four-tensor layer format
+ * [card "...w4a8-convrot-ComfyUI", sections "Format" and "Reproducing"; card
+ * "Qwen3.8-27B-W4A8", section "Model Overview": Hadamard rotation in 256-blocks, then
+ * group quantisation with a 16-level Lloyd-Max codebook, fp8 group scales and fp32
+ * channel scales; the seed pins the codebook fit, which samples].
+ *
+ *  w          [N][K] weights, element type w_dtype (W4A8_F32 or W4A8_BF16)
+ *  N, K       N >= 1; K >= 256 and K % 256 == 0 (the rotation block must divide K)
+ *  seed       seeds the SplitMix64 draw of the 2^20-value fit sample (used when N*K > 2^20)
+ *  packed, s_rel, s_channel, codebook   outputs, layouts as above; codebook ascending
+ *  workspace  device scratch of at least w4a8_quantize_weight_workspace(N, K) bytes
+ *
+ * Steps (all on the device, in stream order): rotate each row by 256-blocks;
+ * s_channel = row max |w_rot|; s_rel = E4M3FN(group max |w_rot| / s_channel), round to
+ * nearest even; v = w_rot / (s_channel * dec(s_rel)); fit 16 levels to v by Lloyd's
+ * iteration in fp64 (mid-quantile start, at most 100 updates); each element takes its
+ * nearest level (ties to the lower index); pack.  Deterministic in (w, N, K, seed).
+ */
+W4A8_API int w4a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, uint64_t seed,
+                         int8_t *packed, uint8_t *s_rel, float *s_channel, float *codebook,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Per-call activation preparation [card "Qwen3.8-27B-W4A8", section "Model Overview":
+ * 4-bit weights with int8 activations; card "...w4a8-convrot-ComfyUI", section "Format":
+ * the layer executes on int8 GEMM in the rotated basis].
+ *
+ *  x      [M][K] activations, element type x_dtype (W4A8_F32 or W4A8_BF16)
+ *  M, K   M >= 1; K >= 256 and K % 256 == 0
+ *  x_q    [M][K] int8 output;  s_x  [M] fp32 output
+ *
+ * Each 256-block of each row is rotated (fp32 fast Hadamard transform, stages of span
+ * 1, 2, ..., 128 in that order, then x 1/16); then per row amax = max |x_rot|,
+ * s_x = amax / 127 and x_q = clamp(rint(x_rot / s_x), -127, 127) with IEEE division and
+ * ties to even; an all-zero row gives s_x = 0 and x_q = 0.  Results are bit-exact and
+ * deterministic.
+ */
+W4A8_API int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *x_q,
+                            float *s_x, void *stream);
+
+/*
+ * The quantised product [card "...w4a8-convrot-ComfyUI", sections "Why this exists"
+ * and "Format": the layer runs on the int8 GEMM path with a codebook dequantisation step
+ * on top; three tiers of scaling -- codebook, group, row].
+ *
+ *  x_q, s_x   prepared activations [M][K], [M] (from w4a8_prepare_activation)
+ *  packed, s_rel, s_channel, codebook   one layer, layouts as above, N rows
+ *  y          [M][N] output, element type y_dtype (W4A8_F32 or W4A8_BF16)
+ *  M >= 1, N >= 1, K >= 256, K % 256 == 0
+ *
+ * Each output satisfies |y - y_exact| <= 4e-3 * sum_k |s_x x_q[k] w_hat[k]| where y_exact
+ * is the fp64 value of the formula above (bf16 output adds its own rounding).  Output is
+ * deterministic: no atomics, fixed reduction order for a given (M, N, K, algorithm).
+ */
+W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
+                const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                void *y, int y_dtype, void *stream);
+
+/* As w4a8_linear with an explicit kernel choice (w4a8_algo).  W4A8_ALGO_GEMV returns
+ * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960). */
+W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
+                     const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
+                     const float *codebook, int64_t N, void *y, int y_dtype, int algo,
+                     void *stream);
+
+/* The algorithm w4a8_linear picks for (M, N, K) on the current device, or a negative
+ * status if the shape is invalid.  Launches nothing. */
+W4A8_API int w4a8_linear_pick(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

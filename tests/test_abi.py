@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/w4a8.h
+declares, and every argument-validation error is returned before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (binds the library's HIP runtime to torch's)
+
+import w4a8_codebook_gemm_amd as w
+from conftest import ROOT
+
+FAKE = 0x10000  # a 16-byte aligned non-null address that is never dereferenced
+MIS = FAKE + 8  # misaligned
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "w4a8.h")).read()
+    return re.findall(r"W4A8_API\s+[\w\s\*]+?\b(w4a8_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w.LIB_PATH):
+        pytest.skip("library not built")
+    return w.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) == 8 and set(names) == set(w.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_exports_nothing_else():
+    out = os.popen(f"nm -D --defined-only {w.LIB_PATH}").read()
+    text = [l.split()[-1] for l in out.splitlines() if " T " in l]
+    assert sorted(text) == sorted(w.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert L.w4a8_version() == 100
+    for s in range(8):
+        assert len(L.w4a8_status_string(s)) > 0
+    assert L.w4a8_status_string(99) == b"unknown status"
+
+
+def test_workspace_size_and_pick(L):
+    assert L.w4a8_quantize_weight_workspace(256, 512) >= 256 * 512 * 4 + 2048 * 4 + (256 * 512 + 1) * 8
+    assert L.w4a8_quantize_weight_workspace(17408, 5120) >= 17408 * 5120 * 4 + (1 << 20) * 12
+    for bad in [(0, 512), (4, 4304), (4, 100), (-1, 256), (4, 0)]:
+        assert L.w4a8_quantize_weight_workspace(*bad) == 0
+    assert L.w4a8_linear_pick(1, 17408, 5120) == w.ALGO_GEMV
+    assert L.w4a8_linear_pick(2, 5120, 17408) == w.ALGO_GEMV
+    assert L.w4a8_linear_pick(2048, 17408, 5120) == w.ALGO_MFMA_I8
+    assert L.w4a8_linear_pick(1, 1, 4304) == -2
+
+
+def lin(L, M=4, K=512, N=256, ptrs=None, ydt=0, algo=0):
+    p = dict(xq=FAKE, sx=FAKE, pk=FAKE, sr=FAKE, sc=FAKE, cb=FAKE, y=FAKE)
+    p.update(ptrs or {})
+    return L.w4a8_linear_algo(p["xq"], p["sx"], M, K, p["pk"], p["sr"], p["sc"], p["cb"], N, p["y"], ydt,
+                              algo, None)
+
+
+def test_linear_validation(L):
+    for k in ("xq", "sx", "pk", "sr", "sc", "cb", "y"):
+        assert lin(L, ptrs={k: 0}) == 1
+    for M, K, N in [(0, 512, 4), (4, 4304, 4), (4, 128, 4), (4, 512, 0), (-3, 512, 4), (4, 0, 4)]:
+        assert lin(L, M=M, K=K, N=N) == 2
+    assert lin(L, ydt=7) == 3
+    assert lin(L, algo=9) == 3
+    for k in ("xq", "sx", "pk", "sr", "sc", "cb", "y"):
+        assert lin(L, ptrs={k: MIS}) == 4
+    assert lin(L, M=8, K=5120, algo=w.ALGO_GEMV) == 2  # outside the GEMV's range
+    assert L.w4a8_linear(0, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == 1
+
+
+def test_prepare_and_quantize_validation(L):
+    assert L.w4a8_prepare_activation(0, 0, 4, 512, FAKE, FAKE, None) == 1
+    assert L.w4a8_prepare_activation(FAKE, 0, 4, 300, FAKE, FAKE, None) == 2
+    assert L.w4a8_prepare_activation(FAKE, 5, 4, 512, FAKE, FAKE, None) == 3
+    assert L.w4a8_prepare_activation(MIS, 0, 4, 512, FAKE, FAKE, None) == 4
+    need = L.w4a8_quantize_weight_workspace(8, 256)
+    q = L.w4a8_quantize_weight
+    assert q(0, 0, 8, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+    assert q(FAKE, 0, 8, 4304, 0, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 2
+    assert q(FAKE, 2, 8, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 3
+    assert q(FAKE, 0, 8, 256, 0, MIS, FAKE, FAKE, FAKE, FAKE, need, None) == 4
+    assert q(FAKE, 0, 8, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 5
+    assert q(FAKE, 0, 8, 256, 0, FAKE, FAKE, FAKE, FAKE, 0, need, None) == 5
+
+
+def test_binding_refuses_cpu_tensors_and_bad_shapes():
+    x = torch.zeros(4, 512)
+    with pytest.raises(ValueError):
+        w.prepare_activation(x)
+    with pytest.raises(ValueError):
+        w.quantize_weight(torch.zeros(4, 512, 3))
+
+
+def test_binding_raises_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(w, "_lib", None)
+    monkeypatch.setattr(w, "LIB_PATH", "/nonexistent/libw4a8.so")
+    with pytest.raises(RuntimeError):
+        w.lib()

@@ -1,0 +1,252 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Integers -- packed indices, e4m3 group-scale bytes, row scales, codebook bits, int8
+activations and their scales -- must match bit for bit.  Products must satisfy
+|y - y_ref| <= 4e-3 * A with y_ref and A = sum_k |s_x x_q w_hat| from the oracle's fp64
+definition; the int8-MFMA path must also match the oracle's int8-codebook value y8 within
+the fp32 rounding of its fold, (G + 4) * 2^-24 * A8 for G = K/16 groups.  Full-size
+shapes are checked on sampled rows and tokens; small shapes span several tiles and ragged
+tails in full.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def w():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a8_codebook_gemm_amd as mod
+    mod.lib()
+    return mod
+
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_layer(N, K, seed=0):
+    W = S.weights(N, K, seed=seed)
+    return W, O.quantize_weight(W, seed=seed)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_acts(M, K, seed=0, n_out=None):
+    x = S.activations(M, K, seed=seed, n_outliers=n_out)
+    xq, sx = O.prepare(x)
+    return x, xq, sx
+
+
+def gpu_layer(w, q):
+    return w.QuantizedLinear(gpu(q["packed"]), gpu(q["s_rel"]), gpu(q["s_ch"]), gpu(q["cb"]))
+
+
+def sample(n, count, seed):
+    if n <= count:
+        return np.arange(n)
+    r = S.u64(seed, 77, count) % np.uint64(n)
+    return np.unique(np.concatenate([[0, n - 1], r.astype(np.int64)]))
+
+
+# ----------------------------------------------------------------------------- prepare
+
+PREP_CASES = [(4, 512, "f32"), (4, 512, "bf16"), (1, 256, "f32"), (3, 5120, "f32"),
+              (2, 17408, "bf16"), (37, 768, "f32"), (5, 20736, "f32"), (2048, 5120, "bf16")]
+
+
+@pytest.mark.parametrize("M,K,dt", PREP_CASES)
+def test_prepare_bit_exact(w, M, K, dt):
+    say(f"prepare M={M} K={K} {dt}")
+    x = S.activations(M, K, seed=M + K, n_outliers=2)
+    if M > 2:
+        x[1] = 0.0                      # all-zero token
+        x[2] = 0.0
+        x[2, K // 3] = -3.0             # a single spike
+    if dt == "bf16":
+        bits = S.to_bf16_bits(x)
+        xin = gpu(bits.view(np.int16)).view(torch.bfloat16)
+        x = S.bf16_bits_to_f32(bits)
+    else:
+        xin = gpu(x)
+    xq_ref, sx_ref = O.prepare(x)
+    xq, sx = w.prepare_activation(xin)
+    torch.cuda.synchronize()
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
+# ----------------------------------------------------------------------------- quantize
+
+def check_quant(w, W, seed, dtype=torch.float32):
+    q = O.quantize_weight(W, seed=seed)
+    Wg = gpu(W) if dtype == torch.float32 else gpu(S.to_bf16_bits(W).view(np.int16)).view(torch.bfloat16)
+    L = w.quantize_weight(Wg, seed=seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(L.codebook.cpu().numpy().view(np.uint32), q["cb"].view(np.uint32))
+    assert np.array_equal(L.s_channel.cpu().numpy().view(np.uint32), q["s_ch"].view(np.uint32))
+    assert np.array_equal(L.s_rel.cpu().numpy(), q["s_rel"])
+    assert np.array_equal(L.packed.cpu().numpy(), q["packed"])
+    return L, q
+
+
+@pytest.mark.parametrize("N,K,seed", [(256, 512, 0), (1, 256, 3), (2048, 1024, 42), (300, 768, 7)])
+def test_quantize_bit_exact(w, N, K, seed):
+    say(f"quantize N={N} K={K} seed={seed}")
+    W = S.weights(N, K, seed=seed)
+    check_quant(w, W, seed)
+
+
+def test_quantize_bf16_input(w):
+    say("quantize bf16 N=64 K=768")
+    W = S.bf16_bits_to_f32(S.to_bf16_bits(S.weights(64, 768, seed=5)))
+    check_quant(w, W, 5, dtype=torch.bfloat16)
+
+
+def test_quantize_constructed_layer_exact(w):
+    from test_oracle import constructed_layer
+    say("quantize constructed layer")
+    W, truth = constructed_layer()
+    L, _ = check_quant(w, W, 0)
+    assert np.array_equal(L.packed.cpu().numpy(), truth["packed"])
+    assert np.array_equal(L.codebook.cpu().numpy(), truth["cb"])
+
+
+@pytest.mark.parametrize("N,K", [S.MLP_GATE_UP, S.MLP_DOWN])
+def test_quantize_full_size(w, N, K):
+    say(f"quantize full N={N} K={K}")
+    W, q = oracle_layer(N, K)
+    L = w.quantize_weight(gpu(W), seed=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(L.codebook.cpu().numpy().view(np.uint32), q["cb"].view(np.uint32))
+    assert np.array_equal(L.s_channel.cpu().numpy().view(np.uint32), q["s_ch"].view(np.uint32))
+    assert np.array_equal(L.s_rel.cpu().numpy(), q["s_rel"])
+    assert np.array_equal(L.packed.cpu().numpy(), q["packed"])
+
+
+# ----------------------------------------------------------------------------- linear
+
+def run_linear(w, algo, N, K, M, rows=None, toks=None, out_dtype=torch.float32, seed=0, n_out=None):
+    _, q = oracle_layer(N, K, seed)
+    _, xq, sx = oracle_acts(M, K, seed, n_out)
+    L = gpu_layer(w, q)
+    y = w.linear(gpu(xq), gpu(sx), L, out_dtype=out_dtype, algo=algo)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    if rows is not None or toks is not None:
+        rr = np.arange(N) if rows is None else rows
+        tt = np.arange(M) if toks is None else toks
+        y = y[np.ix_(tt, rr)]
+    yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, toks)
+    return y, yr, A, (q, xq, sx)
+
+
+def assert_gate(y, yr, A, extra=0.0):
+    err = np.abs(y - yr)
+    bound = 4e-3 * A + extra
+    zero = A == 0
+    assert np.all(y[zero] == 0)
+    ratio = err[~zero] / bound[~zero]
+    say(f"  max |y - y_ref| / (4e-3 A) = {ratio.max():.4f}")
+    assert np.all(err <= bound)
+
+
+GEMV_CASES = [(256, 512, 1), (256, 512, 2), (256, 512, 3), (256, 512, 4), (1001, 768, 3), (1, 256, 1),
+              (8, 10240, 4)]
+
+
+@pytest.mark.parametrize("N,K,M", GEMV_CASES)
+def test_gemv_parity(w, N, K, M):
+    say(f"gemv N={N} K={K} M={M}")
+    y, yr, A, _ = run_linear(w, w.ALGO_GEMV, N, K, M, n_out=2)
+    assert_gate(y, yr, A)
+
+
+@pytest.mark.parametrize("N,K,M", [(17408, 5120, 1), (5120, 17408, 1), (17408, 5120, 2), (5120, 17408, 2)])
+def test_gemv_full_size_sampled(w, N, K, M):
+    say(f"gemv full N={N} K={K} M={M}")
+    rows = sample(N, 2048, N + M)
+    y, yr, A, _ = run_linear(w, w.ALGO_GEMV, N, K, M, rows=rows)
+    assert_gate(y, yr, A)
+
+
+def i8_tight(y, q, xq, sx, rows, toks):
+    y8, A8 = O.linear_i8_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, toks)
+    G = xq.shape[1] // 16
+    err = np.abs(y - y8)
+    bound = (G + 4) * U32 * A8
+    say(f"  max |y - y8| / ((G+4) u A8) = {np.max(err / np.maximum(bound, 1e-300)):.4f}")
+    assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (128, 256, 128)])
+def test_mfma_i8_parity(w, N, K, M):
+    say(f"mfma_i8 N={N} K={K} M={M}")
+    y, yr, A, (q, xq, sx) = run_linear(w, w.ALGO_MFMA_I8, N, K, M, n_out=2)
+    assert_gate(y, yr, A)
+    i8_tight(y, q, xq, sx, None, None)
+
+
+@pytest.mark.parametrize("N,K", [S.MLP_GATE_UP, S.MLP_DOWN])
+def test_mfma_i8_full_size_sampled(w, N, K):
+    M = 2048
+    say(f"mfma_i8 full N={N} K={K} M={M}")
+    rows, toks = sample(N, 384, N), sample(M, 48, M + 1)
+    y, yr, A, (q, xq, sx) = run_linear(w, w.ALGO_MFMA_I8, N, K, M, rows=rows, toks=toks)
+    assert_gate(y, yr, A)
+    i8_tight(y, q, xq, sx, rows, toks)
+
+
+@pytest.mark.parametrize("algo", ["gemv", "mfma_i8"])
+def test_bf16_output(w, algo):
+    a = {"gemv": 1, "mfma_i8": 2}[algo]
+    say(f"bf16 output {algo}")
+    y, yr, A, _ = run_linear(w, a, 256, 512, 2, out_dtype=torch.bfloat16, n_out=2)
+    assert_gate(y, yr, A, extra=2.0 ** -8 * np.abs(yr))
+
+
+@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (0, 1), (0, 300)])
+def test_deterministic_and_auto(w, algo, M):
+    say(f"determinism algo={algo} M={M}")
+    N, K = 512, 1024
+    _, q = oracle_layer(N, K)
+    _, xq, sx = oracle_acts(M, K)
+    L = gpu_layer(w, q)
+    xg, sg = gpu(xq), gpu(sx)
+    a = w.linear(xg, sg, L, algo=algo)
+    b = w.linear(xg, sg, L, algo=algo)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    assert_gate(a.cpu().numpy().astype(np.float64), yr, A)
+
+
+def test_end_to_end_layer_call(w):
+    say("end-to-end layer call")
+    N, K, M = 512, 768, 3
+    W = S.weights(N, K, seed=11)
+    x = S.activations(M, K, seed=11, n_outliers=2)
+    L = w.quantize_weight(gpu(W), seed=11)
+    y = L(gpu(x))
+    torch.cuda.synchronize()
+    q = O.quantize_weight(W, seed=11)
+    xq, sx = O.prepare(x)
+    yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    assert_gate(y.cpu().numpy().astype(np.float64), yr, A)

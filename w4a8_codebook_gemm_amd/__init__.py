@@ -1,0 +1,185 @@
+"""Python binding of libw4a8.so, the MI355X (gfx950) W4A8 codebook linear layer.
+
+Argument marshalling only: every function checks tensor placement, dtype and layout, then
+passes raw device pointers, sizes and the current HIP stream to the C ABI declared in
+include/w4a8.h.  All arithmetic runs in the library's HIP kernels; PyTorch provides device
+memory and streams.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+
+The layer format (model cards "Qwen3.8-27B-uncensored-w4a8-convrot-ComfyUI", section
+"Format"; "Qwen3.8-27B-W4A8 (for ComfyUI)", section "Model Overview"):
+  packed int8 [N, K/2], s_rel uint8 [N, K/16] (E4M3FN bits), s_channel fp32 [N],
+  codebook fp32 [16].
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a8.so")
+
+F32, BF16 = 0, 1
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA_I8, ALGO_MFMA_F16 = 0, 1, 2, 3
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
+          5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
+EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
+           "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
+           "w4a8_linear_algo", "w4a8_linear_pick")
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({lib().w4a8_status_string(status).decode()})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (torch is imported first so HIP resolves to torch's runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python w4a8_codebook_gemm_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        P, i64, u64, i32, sz = C.c_void_p, C.c_int64, C.c_uint64, C.c_int, C.c_size_t
+        L.w4a8_version.restype = i32
+        L.w4a8_status_string.argtypes = [i32]
+        L.w4a8_status_string.restype = C.c_char_p
+        L.w4a8_quantize_weight_workspace.argtypes = [i64, i64]
+        L.w4a8_quantize_weight_workspace.restype = sz
+        L.w4a8_quantize_weight.argtypes = [P, i32, i64, i64, u64, P, P, P, P, P, sz, P]
+        L.w4a8_quantize_weight.restype = i32
+        L.w4a8_prepare_activation.argtypes = [P, i32, i64, i64, P, P, P]
+        L.w4a8_prepare_activation.restype = i32
+        L.w4a8_linear.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i32, P]
+        L.w4a8_linear.restype = i32
+        L.w4a8_linear_algo.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i32, i32, P]
+        L.w4a8_linear_algo.restype = i32
+        L.w4a8_linear_pick.argtypes = [i64, i64, i64]
+        L.w4a8_linear_pick.restype = i32
+        _lib = L
+    return _lib
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _fdtype(t: torch.Tensor) -> int:
+    return BF16 if t.dtype == torch.bfloat16 else F32
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise W4A8Error(status, what)
+
+
+@dataclass
+class QuantizedLinear:
+    """One quantised layer: the four tensors of the format (N rows, K input features)."""
+    packed: torch.Tensor      # int8 [N, K/2]
+    s_rel: torch.Tensor       # uint8 [N, K/16], E4M3FN bit patterns
+    s_channel: torch.Tensor   # float32 [N]
+    codebook: torch.Tensor    # float32 [16]
+
+    @property
+    def out_features(self) -> int:
+        return self.packed.shape[0]
+
+    @property
+    def in_features(self) -> int:
+        return self.packed.shape[1] * 2
+
+    def __call__(self, x: torch.Tensor, out_dtype=torch.float32, algo: int = ALGO_AUTO):
+        x_q, s_x = prepare_activation(x)
+        return linear(x_q, s_x, self, out_dtype=out_dtype, algo=algo)
+
+
+def quantize_weight_workspace(n: int, k: int) -> int:
+    return int(lib().w4a8_quantize_weight_workspace(n, k))
+
+
+def quantize_weight(w: torch.Tensor, seed: int = 0, workspace: torch.Tensor | None = None) -> QuantizedLinear:
+    """Quantise a [N, K] fp32/bf16 weight on the GPU (asynchronous on the current stream)."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    wp = _dev(w, "w", (torch.float32, torch.bfloat16))
+    dev = w.device
+    packed = torch.empty((n, k // 2), dtype=torch.int8, device=dev)
+    s_rel = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    s_ch = torch.empty((n,), dtype=torch.float32, device=dev)
+    cb = torch.empty((16,), dtype=torch.float32, device=dev)
+    need = quantize_weight_workspace(n, k)
+    if need == 0:
+        _check(2, "w4a8_quantize_weight")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    _check(lib().w4a8_quantize_weight(wp, _fdtype(w), n, k, seed & (2**64 - 1), packed.data_ptr(),
+                                      s_rel.data_ptr(), s_ch.data_ptr(), cb.data_ptr(),
+                                      _dev(workspace, "workspace", (torch.uint8,)),
+                                      workspace.numel(), _stream()), "w4a8_quantize_weight")
+    return QuantizedLinear(packed, s_rel, s_ch, cb)
+
+
+def prepare_activation(x: torch.Tensor, out=None):
+    """Rotate and quantise activations [M, K] fp32/bf16 -> (x_q int8 [M, K], s_x fp32 [M])."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    xp = _dev(x, "x", (torch.float32, torch.bfloat16))
+    if out is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
+    else:
+        x_q, s_x = out
+    _check(lib().w4a8_prepare_activation(xp, _fdtype(x), m, k, _dev(x_q, "x_q", (torch.int8,)),
+                                         _dev(s_x, "s_x", (torch.float32,)), _stream()),
+           "w4a8_prepare_activation")
+    return x_q, s_x
+
+
+def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32,
+           algo: int = ALGO_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] = the quantised product of prepared activations with one layer."""
+    m, k = x_q.shape
+    n = layer.packed.shape[0]
+    if (tuple(layer.packed.shape) != (n, k // 2) or tuple(layer.s_rel.shape) != (n, k // 16)
+            or tuple(layer.s_channel.shape) != (n,) or tuple(layer.codebook.shape) != (16,)
+            or tuple(s_x.shape) != (m,)):
+        raise ValueError(f"inconsistent shapes: x_q {tuple(x_q.shape)}, s_x {tuple(s_x.shape)}, "
+                         f"packed {tuple(layer.packed.shape)}, s_rel {tuple(layer.s_rel.shape)}, "
+                         f"s_channel {tuple(layer.s_channel.shape)}, codebook {tuple(layer.codebook.shape)}")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x_q.device)
+    yp = _dev(out, "y", (torch.float32, torch.bfloat16))
+    _check(lib().w4a8_linear_algo(
+        _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
+        _dev(layer.packed, "packed", (torch.int8,)), _dev(layer.s_rel, "s_rel", (torch.uint8,)),
+        _dev(layer.s_channel, "s_channel", (torch.float32,)),
+        _dev(layer.codebook, "codebook", (torch.float32,)), n, yp, _fdtype(out), algo, _stream()),
+        "w4a8_linear")
+    return out
+
+
+def linear_pick(m: int, n: int, k: int) -> int:
+    return int(lib().w4a8_linear_pick(m, n, k))

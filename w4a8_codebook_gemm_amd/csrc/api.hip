@@ -1,0 +1,147 @@
+// C ABI of libw4a8.so: argument validation, device check and kernel dispatch.
+// The public contract (layouts, semantics, error behaviour) is stated in include/w4a8.h.
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/w4a8.h"
+#include "w4a8_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per device: 0 = unknown, 1 = gfx950, 2 = other; CU count cached beside it
+std::atomic<int> g_dev_kind[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+// Resolve the current device once: it must be a gfx950.  Returns a w4a8_status.
+int current_device(int *num_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A8_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return W4A8_ERR_DEVICE;
+    int kind = g_dev_kind[dev].load(std::memory_order_acquire);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return W4A8_ERR_HIP;
+        kind = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_dev_kind[dev].store(kind, std::memory_order_release);
+    }
+    if (kind != 1) return W4A8_ERR_DEVICE;
+    if (num_cu) *num_cu = g_dev_cus[dev].load(std::memory_order_relaxed);
+    return W4A8_OK;
+}
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool valid_k(int64_t K) { return K >= 256 && K % 256 == 0 && K <= (int64_t(1) << 30); }
+inline bool valid_dtype(int d) { return d == W4A8_F32 || d == W4A8_BF16; }
+
+int check_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
+                 const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                 void *y, int y_dtype) {
+    if (!x_q || !s_x || !packed || !s_rel || !s_channel || !codebook || !y) return W4A8_ERR_NULL;
+    if (M < 1 || N < 1 || !valid_k(K) || M > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1)
+        return W4A8_ERR_SHAPE;
+    if (!valid_dtype(y_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(x_q) || !aligned16(s_x) || !aligned16(packed) || !aligned16(s_rel) ||
+        !aligned16(s_channel) || !aligned16(codebook) || !aligned16(y))
+        return W4A8_ERR_ALIGN;
+    return W4A8_OK;
+}
+
+int pick(int64_t M, int64_t K) {
+    if (w4a8::gemv_supported(M, K) && M <= 2) return W4A8_ALGO_GEMV;
+    return W4A8_ALGO_MFMA_I8;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a8_version(void) { return 100; }
+
+const char *w4a8_status_string(int status) {
+    switch (status) {
+        case W4A8_OK: return "ok";
+        case W4A8_ERR_NULL: return "a required pointer is NULL";
+        case W4A8_ERR_SHAPE: return "invalid shape (M, N >= 1; K >= 256 and a multiple of 256)";
+        case W4A8_ERR_DTYPE: return "unknown dtype or algorithm code";
+        case W4A8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case W4A8_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4A8_ERR_HIP: return "HIP runtime call or kernel launch failed";
+        case W4A8_ERR_DEVICE: return "current device is not a gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+size_t w4a8_quantize_weight_workspace(int64_t N, int64_t K) {
+    if (N < 1 || !valid_k(K) || N > (int64_t(1) << 31) - 1) return 0;
+    return w4a8::quantize_workspace_bytes(N, K);
+}
+
+int w4a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, uint64_t seed,
+                         int8_t *packed, uint8_t *s_rel, float *s_channel, float *codebook,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (!w || !packed || !s_rel || !s_channel || !codebook) return W4A8_ERR_NULL;
+    if (N < 1 || !valid_k(K) || N > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
+    if (!valid_dtype(w_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(s_rel) || !aligned16(s_channel) ||
+        !aligned16(codebook))
+        return W4A8_ERR_ALIGN;
+    if (!workspace || workspace_bytes < w4a8::quantize_workspace_bytes(N, K)) return W4A8_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return W4A8_ERR_ALIGN;
+    int st = current_device(nullptr);
+    if (st != W4A8_OK) return st;
+    hipError_t e = w4a8::launch_quantize(w, w_dtype == W4A8_BF16, N, K, seed, packed, s_rel, s_channel,
+                                         codebook, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *x_q,
+                            float *s_x, void *stream) {
+    if (!x || !x_q || !s_x) return W4A8_ERR_NULL;
+    if (M < 1 || !valid_k(K) || M > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
+    if (!valid_dtype(x_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(x_q) || !aligned16(s_x)) return W4A8_ERR_ALIGN;
+    int st = current_device(nullptr);
+    if (st != W4A8_OK) return st;
+    hipError_t e = w4a8::launch_prepare(x, x_dtype == W4A8_BF16, M, K, x_q, s_x,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_linear_pick(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || !valid_k(K)) return -W4A8_ERR_SHAPE;
+    return pick(M, K);
+}
+
+int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
+                     const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
+                     const float *codebook, int64_t N, void *y, int y_dtype, int algo,
+                     void *stream) {
+    int st = check_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype);
+    if (st != W4A8_OK) return st;
+    if (algo == W4A8_ALGO_AUTO) algo = pick(M, K);
+    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8) return W4A8_ERR_DTYPE;
+    if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    w4a8::LinearArgs a{x_q, s_x, M, K, N, packed, s_rel, s_channel, codebook, y, y_dtype == W4A8_BF16};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (algo) {
+        case W4A8_ALGO_GEMV: e = w4a8::launch_gemv(a, num_cu, s); break;
+        default: e = w4a8::launch_gemm_i8(a, s); break;
+    }
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
+                const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                void *y, int y_dtype, void *stream) {
+    return w4a8_linear_algo(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype,
+                            W4A8_ALGO_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal declarations of the gfx950 W4A8 library: launchers and small device helpers.
+// Not part of the public ABI (include/w4a8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+constexpr int kRot = 256;    // rotation block along K
+constexpr int kGroup = 16;   // values per fp8 group scale
+constexpr int kLevels = 16;  // codebook levels
+
+// ---------------------------------------------------------------- e4m3 (OCP E4M3FN)
+// Decode by bit assembly: a normal code (e > 0) is the fp32 with exponent e - 7 + 127 and
+// the 3 mantissa bits on top of the fp32 mantissa; a subnormal code m * 2^-9 is formed as
+// (1 + m/8) * 2^-6 - 2^-6, exact in fp32.  NaN codes are outside the format's use.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t mag = (c & 0x7Fu) << 20;
+    float normal = __uint_as_float(mag + 0x3C000000u);
+    float sub = __uint_as_float(mag + 0x3C800000u) - 0x1p-6f;
+    float v = (c & 0x78u) ? normal : sub;
+    return (c & 0x80u) ? -v : v;
+}
+
+// Round a non-negative finite fp32 to the nearest E4M3FN code, ties to the even code,
+// saturating at 448 (0x7E).  Works on the bit pattern: pick the code exponent, then round
+// the fp32 mantissa to 3 bits (subnormal codes use a fixed 2^-9 quantum).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float x) {
+    if (!(x > 0.0f)) return 0u;              // 0 (and -0)
+    if (x >= 464.0f) return 0x7Eu;           // beyond the 448/480 midpoint: saturate
+    uint32_t b = __float_as_uint(x);
+    int e = (int)(b >> 23) - 127;            // unbiased fp32 exponent (x normal here or tiny)
+    if (e < -6) {                            // code subnormal range: value = m * 2^-9
+        float q = x * 0x1p9f;                // exact scaling by a power of two
+        float r = rintf(q);                  // ties to even
+        return (uint32_t)r;                  // 0..8; 8 == 2^-6 is the first normal code 0x08
+    }
+    uint32_t mant = b & 0x7FFFFFu;
+    uint32_t keep = mant >> 20;              // top 3 mantissa bits
+    uint32_t rest = mant & 0xFFFFFu;         // 20 discarded bits
+    uint32_t half = 0x80000u;
+    uint32_t up = (rest > half) || (rest == half && (keep & 1u));
+    uint32_t code = ((uint32_t)(e + 7) << 3) + keep + up;  // carry into the exponent is right
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// In-place rotation of one 256-block held as 4 consecutive elements per lane of a wave
+// (lane l holds elements 4l..4l+3).  Spans 1 and 2 are in-lane; spans 4..128 exchange with
+// lane ^ 1 .. lane ^ 32.  Each butterfly is one fp32 add (lower element) and one fp32
+// subtract (upper element = lower - upper) in the fixed span order 1, 2, ..., 128; the
+// x 1/16 is exact.  Must be called by all 64 lanes of the wave.
+__device__ __forceinline__ void fwht256_lane4(float v[4], int lane) {
+    // span 1: pairs (0,1), (2,3)
+    float a0 = v[0] + v[1], a1 = v[0] - v[1];
+    float a2 = v[2] + v[3], a3 = v[2] - v[3];
+    // span 2: pairs (0,2), (1,3)
+    v[0] = a0 + a2; v[2] = a0 - a2;
+    v[1] = a1 + a3; v[3] = a1 - a3;
+    // spans 4..128: partner lane = lane ^ s; the lower lane keeps a + b, the upper a - b
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const bool upper = (lane & s) != 0;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            float other = __shfl_xor(v[q], s);
+            v[q] = upper ? (other - v[q]) : (v[q] + other);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) v[q] = v[q] * 0.0625f;
+}
+
+// ---------------------------------------------------------------- misc
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
+hipError_t launch_prepare(const void *x, int x_bf16, int64_t M, int64_t K, int8_t *x_q,
+                          float *s_x, hipStream_t stream);
+
+struct LinearArgs {
+    const int8_t *x_q;
+    const float *s_x;
+    int64_t M, K, N;
+    const int8_t *packed;
+    const uint8_t *s_rel;
+    const float *s_ch;
+    const float *cb;
+    void *y;
+    int y_bf16;
+};
+
+bool gemv_supported(int64_t M, int64_t K);
+hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream);
+hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
+hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
+
+size_t quantize_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint64_t seed,
+                           int8_t *packed, uint8_t *s_rel, float *s_ch, float *cb,
+                           void *workspace, hipStream_t stream);
+
+}  // namespace w4a8
