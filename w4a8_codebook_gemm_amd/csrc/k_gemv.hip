@@ -20,23 +20,38 @@
 //    bits 2..7 in one v_perm, the read is conflict-free, and one v_dot2_f32_f16 with the
 //    fp16 pair of activations (int8 values, exact in fp16) gives two products with fp32
 //    accumulation.  Relative error of the fp16 codebook is at most 2^-11 per level.
+//  * Latency: each 8-lane group keeps two units (512 B) in flight in a register ring
+//    (a unit's slot is refilled with the loads of the unit kDepth ahead as soon as it is
+//    consumed); the first loads go out before the table build; the weight stream uses
+//    non-temporal buffer loads with workgroup-relative 32-bit offsets.
+//  * Units run in row-major order, so a wave reads 1 KiB contiguous per row and its group
+//    scales as one 128-B run; the activation blocks in LDS are padded by 4 words and their
+//    chunks XOR-swizzled per lane so that concurrent reads spread over the banks.
 //  * Each group's two-element dot products are summed in fp32, scaled by the decoded e4m3
 //    group scale, reduced over the 8 lanes with xor shuffles, and written to an LDS
-//    partial per (row, block); one thread per row then sums its partials in block order
-//    and applies s_channel, s_x and the codebook's power-of-two scale.  No atomics: the
-//    result is deterministic.
+//    partial per (row, block) (odd row stride: conflict-free); one thread per row then
+//    sums its partials in block order and applies s_channel (loaded at kernel start), s_x
+//    and the codebook's power-of-two scale.  No atomics: the result is deterministic.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 1024;
 constexpr int kLaneGroups = kThreads / 8;
 constexpr int kTabWords = 256 * 64;                 // 64 KiB
 constexpr int kLdsMax = 160 * 1024;                 // gfx950 LDS per workgroup
 constexpr int kMaxMT = 4;
+constexpr int kMaxXChunks = 40960 / 8 / kThreads;  // 8-value activation chunks per thread
+// Activation words per 256-wide K block in LDS: 128 fp16 pairs + 4 words of padding, so
+// lane groups reading consecutive blocks start on different banks.
+constexpr int kXBlk = 132;
+
+template <int MT>
+constexpr int depth() { return 2; }  // units in flight per 8-lane group (more only adds contention)
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
@@ -47,121 +62,247 @@ __device__ __forceinline__ uint32_t tab_read(const uint32_t *lds, uint32_t byte_
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds) + byte_addr);
 }
 
-// 16 packed bytes of one row against MT token vectors: two groups of 16 products each.
+// Both rows of a unit (2 x 16 packed bytes) against MT token vectors.  All 32 table reads
+// are issued before the first dot product so one LDS round trip covers the whole unit;
+// each group's 8 products are split over two accumulators to shorten the dependency
+// chain.  g[row][group] receives the group partials.
 template <int MT>
-__device__ __forceinline__ void row_block(const uint32_t *lds, uint32_t lanebase, const uint4 &p,
-                                          const uint32_t (&xv)[MT][16], float (&g0)[MT],
-                                          float (&g1)[MT]) {
-    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+__device__ __forceinline__ void unit_dots(const uint32_t *lds, uint32_t lanebase, const u32x4 &pa,
+                                          const u32x4 &pb, const uint32_t (&xv)[MT][16],
+                                          float (&g)[MT][2][2]) {
+    const uint32_t w[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    uint32_t pair[32];
 #pragma unroll
-    for (int m = 0; m < MT; m++) g0[m] = g1[m] = 0.0f;
+    for (int i = 0; i < 32; i++)
+        pair[i] = tab_read(lds, __builtin_amdgcn_perm(lanebase, w[i >> 2], 0x0C0C0004u | ((i & 3) << 8)));
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-        const uint32_t addr = __builtin_amdgcn_perm(lanebase, w[i >> 2], 0x0C0C0004u | ((i & 3) << 8));
-        const uint32_t pair = tab_read(lds, addr);
+    for (int m = 0; m < MT; m++) {
 #pragma unroll
-        for (int m = 0; m < MT; m++) {
-            if (i < 8) g0[m] = dot2(pair, xv[m][i], g0[m]);
-            else g1[m] = dot2(pair, xv[m][i], g1[m]);
+        for (int r = 0; r < 2; r++) {
+#pragma unroll
+            for (int gi = 0; gi < 2; gi++) {
+                float e0 = 0.0f, e1 = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 8; q += 2) {
+                    e0 = dot2(pair[16 * r + 8 * gi + q], xv[m][8 * gi + q], e0);
+                    e1 = dot2(pair[16 * r + 8 * gi + q + 1], xv[m][8 * gi + q + 1], e1);
+                }
+                g[m][r][gi] = e0 + e1;
+            }
         }
     }
 }
 
+// 8-lane sum with DPP adds (no LDS traffic): lanes of a quad exchange over distances 1 and
+// 2, then lane 8k adds the quad of lane 8k+4 (row rotate by 12).  Lane 8k ends with the
+// sum of lanes 8k..8k+7.
+__device__ __forceinline__ float sum8_to_leader(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x12C, 0xF, 0xF, false));  // row_ror:12
+    return v;
+}
+
+// One ring slot: buffer offsets of a unit for this lane, where its activations and partial
+// live in LDS, and whether it exists.
+struct Slot {
+    uint32_t op, os;   // byte offsets of row 2rp's packed indices / group scales (this lane)
+    int xw, pidx;      // LDS word of this lane's activation slot; partial index of row 2rp
+    bool valid;
+};
+
 template <int MT>
 __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg) {
-    extern __shared__ uint32_t lds[];
+    // The pair table is a static LDS array at a compile-time address, so each lookup is one
+    // v_perm for the address and one ds_read_b32; activations and partials follow it in
+    // dynamic LDS.
+    __shared__ __align__(16) uint32_t lds[kTabWords];
+    extern __shared__ uint32_t dyn[];
     const int tid = threadIdx.x;
     const int64_t K = a.K, N = a.N;
     const int nblk = (int)(K / kRot);
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
     const int nrow = (int)min((int64_t)rows_per_wg, N - r0);
-    uint32_t *xs = lds + kTabWords;                              // [MT][K/2] fp16 pairs
-    float *part = reinterpret_cast<float *>(xs + MT * (K / 2));  // [MT][rows_per_wg][nblk]
+    const int P = (nrow + 1) >> 1;                               // row pairs
+    const int units = P * nblk;
+    const int pstride = nblk | 1;                                // odd: conflict-free row sums
+    const int xtok = nblk * kXBlk;                               // LDS words per token
+    uint32_t *xs = dyn;                                          // [MT][nblk][kXBlk] fp16 pairs
+    float *part = reinterpret_cast<float *>(xs + MT * xtok);     // [MT][rows_per_wg][pstride]
 
-    // codebook -> fp16 pair table, scaled by 2^-ex with max |cb| = f * 2^ex, f in [0.5, 1)
+    const int j = tid & 7;
+    const uint32_t lanebase = (uint32_t)(tid & 63) * 4u;
+    const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
+    // Workgroup-relative 32-bit offsets into buffer resources bounded by this workgroup's
+    // rows: row 2rp+1 past the last row reads as zero and is never stored.
+    const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.packed + r0 * rowbytes), (short)0, (int)(nrow * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.s_rel + r0 * grpbytes), (short)0, (int)(nrow * grpbytes), 0x00020000);
+    constexpr int kNT = 2;  // non-temporal: the weights are streamed once per call
+
+    // Units in row-major order u = rp * nblk + t; lane group g of wave w takes units
+    // 8w + g + 128 i.  The wave's base unit b = 8w + 128 i is uniform: its position
+    // (rpb, tb) lives in scalar registers and advances by 128 units per step; each lane
+    // adds a constant delta for its g (at most one row wrap, since g % nblk < nblk).
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = (tid >> 3) & 7;
+    const int gdiv = g / nblk, gmod = g - gdiv * nblk;
+    const uint32_t dop = (uint32_t)gdiv * 2u * rowbytes + (uint32_t)gmod * 128u + 16u * j;
+    const uint32_t dos = (uint32_t)gdiv * 2u * grpbytes + (uint32_t)gmod * 16u + 2u * j;
+    const int dpidx = gdiv * 2 * pstride + gmod, dxw = gmod * kXBlk + 16 * j;
+    const int sdrp = kLaneGroups / nblk, sdt = kLaneGroups - sdrp * nblk;
+    int bu = 8 * wave;                       // wave base unit (uniform)
+    int rpb = bu / nblk, tb = bu - rpb * nblk;
+    auto make_slot = [&]() {
+        Slot sl;
+        const bool wrap = tb + gmod >= nblk;
+        sl.valid = bu + g < units;
+        const uint32_t opb = (uint32_t)rpb * 2u * rowbytes + (uint32_t)tb * 128u + dop;
+        const uint32_t osb = (uint32_t)rpb * 2u * grpbytes + (uint32_t)tb * 16u + dos;
+        sl.op = wrap ? opb + rowbytes : opb;   // wrap: next row pair, t - nblk
+        sl.os = wrap ? osb + grpbytes : osb;
+        const int pb_ = rpb * 2 * pstride + tb * 1 + dpidx, xb = tb * kXBlk + dxw;
+        sl.pidx = wrap ? pb_ + 2 * pstride - nblk : pb_;
+        sl.xw = wrap ? xb - nblk * kXBlk : xb;
+        return sl;
+    };
+    auto step = [&]() {
+        bu += kLaneGroups;
+        tb += sdt;
+        rpb += sdrp;
+        if (tb >= nblk) { tb -= nblk; rpb += 1; }
+    };
+
+    // Loads are issued unconditionally (a fixed count per ring slot keeps the hardware's
+    // in-order load counter exact); a unit past the end gets an offset beyond the buffer,
+    // which reads as zero without touching memory.
+    constexpr uint32_t kOutside = 0x80000000u;
+    auto fetch = [&](const Slot &sl, u32x4 &pa, u32x4 &pb, uint32_t &sa, uint32_t &sb) {
+        const uint32_t op = sl.valid ? sl.op : kOutside, os = sl.valid ? sl.os : kOutside;
+        pa = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op, 0, kNT);
+        pb = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op + rowbytes, 0, kNT);
+        sa = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os, 0, kNT);
+        sb = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os + grpbytes, 0, kNT);
+    };
+
+    // Small operands first: the row scales of this workgroup's rows (one per thread, kept
+    // in a register until the final sums), and the activations.  Their loads precede the
+    // weight loads in the in-order load counter, so using them does not wait for the
+    // weight prefetch.
+    const float sch_mine = tid < nrow ? a.s_ch[r0 + tid] : 0.0f;
+    const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
+    const int nxc = (int)(MT * (K / 8));
+    uint2 xraw[kMaxXChunks];
+#pragma unroll
+    for (int q = 0; q < kMaxXChunks; q++) {
+        const int i = tid + q * kThreads;
+        xraw[q] = i < nxc ? xq8[i] : make_uint2(0, 0);
+    }
+
+    // A ring of kDepth units in flight per lane group; the first loads are issued before
+    // the prologue so their HBM latency overlaps the table build.
+    constexpr int kDepth = depth<MT>();
+    Slot cur[kDepth];
+    u32x4 pa[kDepth], pb[kDepth];
+    uint32_t sa[kDepth], sb[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; d++) {
+        cur[d] = make_slot();
+        fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
+        step();
+    }
+
+    // codebook -> fp16 pair table, scaled by 2^-ex with max |cb| = f * 2^ex, f in [0.5, 1).
+    // Wave w writes entries 16w .. 16w+15 (high nibble w), each lane its own column.
     float cmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kLevels; j++) cmax = fmaxf(cmax, fabsf(a.cb[j]));
+    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(a.cb[q]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
     const float inv = ldexpf(1.0f, -ex);
-    uint32_t h[kLevels];
+    {
+        static_assert(kThreads / 64 == kLevels, "one wave per high nibble");
+        const int w = tid >> 6, lane = tid & 63;
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[w] * inv));
 #pragma unroll
-    for (int j = 0; j < kLevels; j++)
-        h[j] = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[j] * inv));
-    for (int i = tid; i < kTabWords; i += kThreads) {
-        const int e = i >> 6;
-        lds[i] = h[e & 15] | (h[e >> 4] << 16);
+        for (int lo = 0; lo < kLevels; lo++) {
+            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[lo] * inv)) | (hi << 16);
+            lds[(16 * w + lo) * 64 + lane] = v;
+        }
     }
-    // activations int8 -> fp16 pairs (exact)
-    const uint32_t *xq4 = reinterpret_cast<const uint32_t *>(a.x_q);
-    for (int64_t i = tid; i < MT * (K / 4); i += kThreads) {
-        const uint32_t w = xq4[i];
-        uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(int8_t)(w & 0xFF)) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((w >> 8) & 0xFF)) << 16);
-        uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(int8_t)((w >> 16) & 0xFF)) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)(w >> 24)) << 16);
-        xs[2 * i] = lo;
-        xs[2 * i + 1] = hi;
+    // activations int8 -> fp16 pairs (exact), one 4-word chunk (8 values) per item, stored
+    // at chunk c ^ ((j >> 1) & 3) of its 16-word lane slot j so that the 8 lanes of a group
+    // reading their chunk c hit distinct banks
+#pragma unroll
+    for (int q = 0; q < kMaxXChunks; q++) {
+        const int i = tid + q * kThreads;
+        if (i < nxc) {
+            const uint2 w = xraw[q];
+            auto cvt2 = [](uint32_t v, int sh) {
+                return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> sh) & 0xFF)) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> (sh + 8)) & 0xFF)) << 16);
+            };
+            const int word = 4 * i;  // logical word of this chunk (token m = word / (K/2))
+            const int m = word / (int)(K / 2), wk = word - m * (int)(K / 2);
+            const int d = wk & 127, lj = d >> 4, c = (d >> 2) & 3;
+            const int phys = m * xtok + (wk >> 7) * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2);
+            *reinterpret_cast<uint4 *>(xs + phys) = make_uint4(cvt2(w.x, 0), cvt2(w.x, 16), cvt2(w.y, 0), cvt2(w.y, 16));
+        }
     }
     __syncthreads();
 
-    const int lg = tid >> 3, j = tid & 7;
-    const uint32_t lanebase = (uint32_t)(tid & 63) * 4u;
-    const int npairs = (nrow + 1) >> 1;
-    const int units = npairs * nblk;
-    const int64_t rowbytes = K / 2, grpbytes = K / kGroup;
-    for (int u = lg; u < units; u += kLaneGroups) {
-        const int rp = u / nblk, t = u - rp * nblk;
-        const int rla = 2 * rp, rlb = rla + 1;
-        const bool hasb = rlb < nrow;
-        const int64_t ra = r0 + rla, rb = hasb ? ra + 1 : ra;
-        const int64_t koff = (int64_t)t * 128 + 16 * j;
-        const uint4 pa = *reinterpret_cast<const uint4 *>(a.packed + ra * rowbytes + koff);
-        const uint4 pb = *reinterpret_cast<const uint4 *>(a.packed + rb * rowbytes + koff);
-        const uint32_t sa = *reinterpret_cast<const uint16_t *>(a.s_rel + ra * grpbytes + t * 16 + 2 * j);
-        const uint32_t sb = *reinterpret_cast<const uint16_t *>(a.s_rel + rb * grpbytes + t * 16 + 2 * j);
+    const int xsw = (j >> 1) & 3;
+    auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb, uint32_t sa, uint32_t sb) {
+        const int xbase = sl.xw;
         uint32_t xv[MT][16];
 #pragma unroll
         for (int m = 0; m < MT; m++) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(xs + m * (K / 2) + koff);
 #pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const uint4 v = src[c];
-                xv[m][4 * c + 0] = v.x; xv[m][4 * c + 1] = v.y;
-                xv[m][4 * c + 2] = v.z; xv[m][4 * c + 3] = v.w;
+            for (int q = 0; q < 4; q++) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * xtok + xbase + 4 * (q ^ xsw));
+                xv[m][4 * q + 0] = v.x; xv[m][4 * q + 1] = v.y;
+                xv[m][4 * q + 2] = v.z; xv[m][4 * q + 3] = v.w;
             }
         }
-        float ga0[MT], ga1[MT], gb0[MT], gb1[MT];
-        row_block<MT>(lds, lanebase, pa, xv, ga0, ga1);
-        row_block<MT>(lds, lanebase, pb, xv, gb0, gb1);
-        const float sa0 = e4m3_to_f32(sa & 0xFF), sa1 = e4m3_to_f32(sa >> 8);
-        const float sb0 = e4m3_to_f32(sb & 0xFF), sb1 = e4m3_to_f32(sb >> 8);
+        float g[MT][2][2];
+        unit_dots<MT>(lds, lanebase, pa, pb, xv, g);
+        // gfx950's v_cvt_f32_fp8 decodes OCP E4M3FN (checked on all 254 finite codes)
+        const float fa0 = __builtin_amdgcn_cvt_f32_fp8((int)sa, 0), fa1 = __builtin_amdgcn_cvt_f32_fp8((int)sa, 1);
+        const float fb0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0), fb1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
 #pragma unroll
         for (int m = 0; m < MT; m++) {
-            float va = sa0 * ga0[m] + sa1 * ga1[m];
-            float vb = sb0 * gb0[m] + sb1 * gb1[m];
-#pragma unroll
-            for (int s = 1; s < 8; s <<= 1) {
-                va += __shfl_xor(va, s);
-                vb += __shfl_xor(vb, s);
-            }
+            const float va = sum8_to_leader(fmaf(fa1, g[m][0][1], fa0 * g[m][0][0]));
+            const float vb = sum8_to_leader(fmaf(fb1, g[m][1][1], fb0 * g[m][1][0]));
             if (j == 0) {
-                part[(m * rows_per_wg + rla) * nblk + t] = va;
-                if (hasb) part[(m * rows_per_wg + rlb) * nblk + t] = vb;
+                float *pp = part + m * rows_per_wg * pstride + sl.pidx;
+                pp[0] = va;
+                pp[pstride] = vb;  // an odd last row pair writes row nrow < rows_per_wg, never read
             }
+        }
+    };
+
+    while (__builtin_amdgcn_readfirstlane(bu) - kDepth * kLaneGroups < units) {
+#pragma unroll
+        for (int d = 0; d < kDepth; d++) {
+            if (cur[d].valid) compute(cur[d], pa[d], pb[d], sa[d], sb[d]);
+            cur[d] = make_slot();
+            fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
+            step();
         }
     }
     __syncthreads();
 
+    // one thread per (token, row): sum the row's block partials in block order
     const float cbscale = ldexpf(1.0f, ex);
     for (int i = tid; i < MT * nrow; i += kThreads) {
         const int m = i / nrow, rl = i - m * nrow;
-        const float *pp = part + (m * rows_per_wg + rl) * nblk;
+        const float *pp = part + (m * rows_per_wg + rl) * pstride;
         float acc = 0.0f;
         for (int t = 0; t < nblk; t++) acc += pp[t];
+        const float sch = (i < kThreads && m == 0) ? sch_mine : a.s_ch[r0 + rl];
         const int64_t r = r0 + rl;
-        const float v = ((acc * a.s_ch[r]) * a.s_x[m]) * cbscale;
+        const float v = ((acc * sch) * a.s_x[m]) * cbscale;
         if (a.y_bf16)
             static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(v);
         else
@@ -172,16 +313,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
 template <int MT>
 hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
     const int64_t nblk = a.K / kRot;
-    const int64_t fixed = (int64_t)kTabWords * 4 + (int64_t)MT * a.K * 2;
+    const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4;  // dynamic part; the 64 KiB table is static
     int64_t rows = (a.N + num_cu - 1) / num_cu;
     rows += rows & 1;
-    while (rows > 2 && fixed + (int64_t)MT * rows * nblk * 4 > kLdsMax) rows = ((rows / 2) + 1) & ~1LL;
-    const int64_t lds = fixed + (int64_t)MT * rows * nblk * 4;
-    if (lds > kLdsMax) return hipErrorInvalidValue;
+    const int64_t dyn_max = kLdsMax - (int64_t)kTabWords * 4;
+    const int64_t pstride = nblk | 1;
+    while (rows > 2 && fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) rows = ((rows / 2) + 1) & ~1LL;
+    const int64_t lds = fixed + (int64_t)MT * rows * pstride * 4;
+    if (lds > dyn_max) return hipErrorInvalidValue;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(kLdsMax - kTabWords * 4));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
