@@ -149,12 +149,18 @@ def main():
     ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
 
     def step(c):
+        """The decode hot path for one token on both shapes: rotation + int8 quantisation +
+        W4A8 product, fused into one launch per matrix."""
+        for sh in shapes:
+            w.forward(xs[sh], layers[sh][c], out=ys[sh], x_q=xqs[sh][0], s_x=xqs[sh][1])
+
+    def step_unfused(c):
         for sh in shapes:
             w.prepare_activation(xs[sh], out=xqs[sh])
             w.linear(*xqs[sh], layers[sh][c], out=ys[sh])
 
-    def step_graph(cs):
-        return make_graph(torch, lambda: [step(c) for c in cs])
+    def step_graph(cs, fn=step):
+        return make_graph(torch, lambda: [fn(c) for c in cs])
 
     full = step_graph(range(COPIES))
     rem = args.steps % COPIES
@@ -178,6 +184,9 @@ def main():
     wb = sum(weight_bytes(n, k) for (n, k) in shapes)
     value = wb / (el / args.steps) / 1e9
     log(f"decode step: {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth")
+    unf = step_graph(range(COPIES), step_unfused)
+    t_unf = time_graph_launches(torch, unf, COPIES, max(4, args.steps // (4 * COPIES)))
+    log(f"decode step with separate prepare launches: {t_unf * 1e6:.2f} us")
 
     # the dominant kernel: decode GEMV, back-to-back launches over the 16 distinct matrices
     for sh in shapes:
@@ -200,10 +209,12 @@ def main():
         "steps": args.steps, "warmup": warm, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "decode M=1: prepare + linear, gate/up 17408x5120 and down 5120x17408, "
+        "config": {"workload": "decode M=1: rotate + int8-quantise + W4A8 product (w4a8_forward), "
+                               "gate/up 17408x5120 and down 5120x17408, "
                                f"{COPIES} distinct weight copies per shape",
                    "tokens": 1, "weight_bytes_per_step": wb},
         "tokens_per_s": round(1.0 / (el / args.steps), 1),
+        "unfused_step_us": round(t_unf * 1e6, 2),
         "roofline": roofline,
     }
 

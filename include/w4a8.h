@@ -148,6 +148,20 @@ W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, in
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,
                      void *stream);
 
+/*
+ * Activation preparation and product in one call: the same results as
+ * w4a8_prepare_activation(x -> x_q, s_x) followed by w4a8_linear(x_q, s_x -> y), bit for
+ * bit in x_q and s_x and within the same bound in y.  For decode sizes (M <= 2 and
+ * K <= 20480) both run in ONE kernel launch: the GEMV's workgroups rotate and quantise
+ * the activations in their prologue [card "...w4a8-convrot-ComfyUI", section "Why this
+ * exists": every generated token re-reads all weights, so per-token fixed costs matter];
+ * otherwise the two steps run as separate launches.  x_q [M][K] and s_x [M] are
+ * caller-provided outputs in both cases.  Argument rules as for the two calls.
+ */
+W4A8_API int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *packed,
+                          const uint8_t *s_rel, const float *s_channel, const float *codebook,
+                          int64_t N, void *y, int y_dtype, int8_t *x_q, float *s_x, void *stream);
+
 /* The algorithm w4a8_linear picks for (M, N, K) on the current device, or a negative
  * status if the shape is invalid.  Launches nothing. */
 W4A8_API int w4a8_linear_pick(int64_t M, int64_t N, int64_t K);

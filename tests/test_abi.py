@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 8 and set(names) == set(w.EXPORTS)
+    assert len(names) == 9 and set(names) == set(w.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 
@@ -105,3 +105,17 @@ def test_binding_raises_loudly_without_library(monkeypatch):
     monkeypatch.setattr(w, "LIB_PATH", "/nonexistent/libw4a8.so")
     with pytest.raises(RuntimeError):
         w.lib()
+
+
+def test_forward_validation(L):
+    f = L.w4a8_forward
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("xdt", 0), kw.get("M", 1), kw.get("K", 512), FAKE, FAKE, FAKE,
+                         FAKE, kw.get("N", 256), FAKE, 0, kw.get("xq", FAKE), kw.get("sx", FAKE), None]
+    assert f(*args(x=0)) == 1
+    assert f(*args(xq=0)) == 1
+    assert f(*args(sx=0)) == 1
+    assert f(*args(K=4304)) == 2
+    assert f(*args(M=0)) == 2
+    assert f(*args(xdt=4)) == 3
+    assert f(*args(x=MIS)) == 4
+    assert f(*args(xq=MIS)) == 4

@@ -250,3 +250,34 @@ def test_end_to_end_layer_call(w):
     xq, sx = O.prepare(x)
     yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
     assert_gate(y.cpu().numpy().astype(np.float64), yr, A)
+
+
+FWD_CASES = [(256, 512, 1, "f32"), (256, 512, 2, "bf16"), (1001, 768, 1, "bf16"), (64, 20480, 1, "f32"),
+             (8, 20480, 2, "f32"), (300, 256, 2, "f32"), (200, 1024, 7, "f32"), (128, 20736, 1, "bf16")]
+
+
+@pytest.mark.parametrize("N,K,M,dt", FWD_CASES)
+def test_forward_fused_and_fallback(w, N, K, M, dt):
+    """w4a8_forward: x_q and s_x bit-exact with the oracle's preparation, y within the bound
+    (one launch for M <= 2 and K <= 20480, two launches otherwise)."""
+    say(f"forward N={N} K={K} M={M} {dt}")
+    _, q = oracle_layer(N, K, 3)
+    x = S.activations(M, K, seed=N + K + M, n_outliers=2)
+    if M > 1:
+        x[1] = 0.0  # an all-zero token
+    if dt == "bf16":
+        bits = S.to_bf16_bits(x)
+        xin = gpu(bits.view(np.int16)).view(torch.bfloat16)
+        x = S.bf16_bits_to_f32(bits)
+    else:
+        xin = gpu(x)
+    xq_ref, sx_ref = O.prepare(x)
+    L = gpu_layer(w, q)
+    x_q = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    s_x = torch.empty((M,), dtype=torch.float32, device=DEV)
+    y = w.forward(xin, L, x_q=x_q, s_x=s_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(x_q.cpu().numpy(), xq_ref)
+    yr, A = O.linear_ref(xq_ref, sx_ref, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    assert_gate(y.cpu().numpy().astype(np.float64), yr, A)

@@ -28,7 +28,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN"
           5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
            "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
-           "w4a8_linear_algo", "w4a8_linear_pick")
+           "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward")
 
 
 class W4A8Error(RuntimeError):
@@ -64,6 +64,8 @@ def lib():
         L.w4a8_linear_algo.restype = i32
         L.w4a8_linear_pick.argtypes = [i64, i64, i64]
         L.w4a8_linear_pick.restype = i32
+        L.w4a8_forward.argtypes = [P, i32, i64, i64, P, P, P, P, i64, P, i32, P, P, P]
+        L.w4a8_forward.restype = i32
         _lib = L
     return _lib
 
@@ -110,6 +112,8 @@ class QuantizedLinear:
         return self.packed.shape[1] * 2
 
     def __call__(self, x: torch.Tensor, out_dtype=torch.float32, algo: int = ALGO_AUTO):
+        if algo == ALGO_AUTO:
+            return forward(x, self, out_dtype=out_dtype)
         x_q, s_x = prepare_activation(x)
         return linear(x_q, s_x, self, out_dtype=out_dtype, algo=algo)
 
@@ -178,6 +182,34 @@ def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dty
         _dev(layer.s_channel, "s_channel", (torch.float32,)),
         _dev(layer.codebook, "codebook", (torch.float32,)), n, yp, _fdtype(out), algo, _stream()),
         "w4a8_linear")
+    return out
+
+
+def forward(x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32, out=None,
+            x_q: torch.Tensor | None = None, s_x: torch.Tensor | None = None) -> torch.Tensor:
+    """prepare_activation + linear in one call (one kernel launch for decode sizes).
+    x_q [M, K] int8 and s_x [M] fp32 receive the prepared activations."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    n = layer.packed.shape[0]
+    if (tuple(layer.packed.shape) != (n, k // 2) or tuple(layer.s_rel.shape) != (n, k // 16)
+            or tuple(layer.s_channel.shape) != (n,) or tuple(layer.codebook.shape) != (16,)):
+        raise ValueError("layer tensors do not match x's in_features")
+    xp = _dev(x, "x", (torch.float32, torch.bfloat16))
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _check(lib().w4a8_forward(xp, _fdtype(x), m, k, _dev(layer.packed, "packed", (torch.int8,)),
+                              _dev(layer.s_rel, "s_rel", (torch.uint8,)),
+                              _dev(layer.s_channel, "s_channel", (torch.float32,)),
+                              _dev(layer.codebook, "codebook", (torch.float32,)), n,
+                              _dev(out, "y", (torch.float32, torch.bfloat16)), _fdtype(out),
+                              _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)),
+                              _stream()), "w4a8_forward")
     return out
 
 

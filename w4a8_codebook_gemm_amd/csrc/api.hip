@@ -127,13 +127,36 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A8_OK) return st;
-    w4a8::LinearArgs a{x_q, s_x, M, K, N, packed, s_rel, s_channel, codebook, y, y_dtype == W4A8_BF16};
+    w4a8::LinearArgs a{x_q, s_x, M, K, N, packed, s_rel, s_channel, codebook, y, y_dtype == W4A8_BF16,
+                       nullptr, 0, nullptr, nullptr};
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     switch (algo) {
         case W4A8_ALGO_GEMV: e = w4a8::launch_gemv(a, num_cu, s); break;
         default: e = w4a8::launch_gemm_i8(a, s); break;
     }
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t *packed,
+                 const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                 void *y, int y_dtype, int8_t *x_q, float *s_x, void *stream) {
+    if (!x) return W4A8_ERR_NULL;
+    int st = check_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype);
+    if (st != W4A8_OK) return st;
+    if (!valid_dtype(x_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(x)) return W4A8_ERR_ALIGN;
+    if (!(w4a8::gemv_fused_supported(M, K) && pick(M, K) == W4A8_ALGO_GEMV)) {
+        st = w4a8_prepare_activation(x, x_dtype, M, K, x_q, s_x, stream);
+        if (st != W4A8_OK) return st;
+        return w4a8_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype, stream);
+    }
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    w4a8::LinearArgs a{x_q, s_x, M, K, N, packed, s_rel, s_channel, codebook, y, y_dtype == W4A8_BF16,
+                       x, x_dtype == W4A8_BF16, x_q, s_x};
+    hipError_t e = w4a8::launch_gemv_fused(a, num_cu, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 

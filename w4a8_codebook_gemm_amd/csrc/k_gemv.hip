@@ -49,6 +49,9 @@ constexpr int kMaxXChunks = 40960 / 8 / kThreads;  // 8-value activation chunks 
 // Activation words per 256-wide K block in LDS: 128 fp16 pairs + 4 words of padding, so
 // lane groups reading consecutive blocks start on different banks.
 constexpr int kXBlk = 132;
+// Fused activation preparation keeps a token's rotated row in registers: 16 waves x 5
+// blocks of 256, so K <= 20480.
+constexpr int kFusedBlocks = 5;
 
 template <int MT>
 constexpr int depth() { return 2; }  // units in flight per 8-lane group (more only adds contention)
@@ -111,7 +114,11 @@ struct Slot {
     bool valid;
 };
 
-template <int MT>
+// XIN selects the activation input: 0 = prepared int8 x_q and s_x; 1 = fp32 and 2 = bf16
+// raw activations, rotated and quantised in the prologue with the arithmetic of the
+// activation kernel (every workgroup does the same, bit for bit; workgroup 0 also stores
+// x_q and s_x).
+template <int MT, int XIN>
 __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg) {
     // The pair table is a static LDS array at a compile-time address, so each lookup is one
     // v_perm for the address and one ds_read_b32; activations and partials follow it in
@@ -191,13 +198,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     // weight loads in the in-order load counter, so using them does not wait for the
     // weight prefetch.
     const float sch_mine = tid < nrow ? a.s_ch[r0 + tid] : 0.0f;
+    float sx_all[MT];
     const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
     const int nxc = (int)(MT * (K / 8));
-    uint2 xraw[kMaxXChunks];
+    uint2 xraw[XIN == 0 ? kMaxXChunks : 1];
+    float xr[XIN == 0 ? 1 : MT][kFusedBlocks][4];  // raw activations: wave w holds blocks w + 16 i
+    const int lane64 = tid & 63, wave64 = tid >> 6;
+    if constexpr (XIN == 0) {
 #pragma unroll
-    for (int q = 0; q < kMaxXChunks; q++) {
-        const int i = tid + q * kThreads;
-        xraw[q] = i < nxc ? xq8[i] : make_uint2(0, 0);
+        for (int m = 0; m < MT; m++) sx_all[m] = a.s_x[m];
+#pragma unroll
+        for (int q = 0; q < kMaxXChunks; q++) {
+            const int i = tid + q * kThreads;
+            xraw[q] = i < nxc ? xq8[i] : make_uint2(0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < MT; m++)
+#pragma unroll
+            for (int i = 0; i < kFusedBlocks; i++) {
+                const int b = wave64 + 16 * i;
+                if (b < nblk) load4<XIN == 2>(a.x_raw, m * K + (int64_t)b * kRot + 4 * lane64, xr[m][i]);
+            }
     }
 
     // A ring of kDepth units in flight per lane group; the first loads are issued before
@@ -231,23 +253,66 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
             lds[(16 * w + lo) * 64 + lane] = v;
         }
     }
-    // activations int8 -> fp16 pairs (exact), one 4-word chunk (8 values) per item, stored
-    // at chunk c ^ ((j >> 1) & 3) of its 16-word lane slot j so that the 8 lanes of a group
-    // reading their chunk c hit distinct banks
+    auto cvt2 = [](uint32_t v, int sh) {
+        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> sh) & 0xFF)) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> (sh + 8)) & 0xFF)) << 16);
+    };
+    if constexpr (XIN == 0) {
+        // activations int8 -> fp16 pairs (exact), one 4-word chunk (8 values) per item, stored
+        // at chunk c ^ ((j >> 1) & 3) of its 16-word lane slot j so that the 8 lanes of a group
+        // reading their chunk c hit distinct banks
+    #pragma unroll
+        for (int q = 0; q < kMaxXChunks; q++) {
+            const int i = tid + q * kThreads;
+            if (i < nxc) {
+                const uint2 w = xraw[q];
+                const int word = 4 * i;  // logical word of this chunk (token m = word / (K/2))
+                const int m = word / (int)(K / 2), wk = word - m * (int)(K / 2);
+                const int d = wk & 127, lj = d >> 4, c = (d >> 2) & 3;
+                const int phys = m * xtok + (wk >> 7) * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2);
+                *reinterpret_cast<uint4 *>(xs + phys) = make_uint4(cvt2(w.x, 0), cvt2(w.x, 16), cvt2(w.y, 0), cvt2(w.y, 16));
+            }
+        }
+    } else {
+        // rotate, per-token amax over the workgroup, quantise; fp16 pairs into the swizzled
+        // layout; workgroup 0 also stores x_q and s_x
+        float *red = part + MT * rows_per_wg * pstride;  // [MT][16] wave maxima (dynamic LDS tail)
 #pragma unroll
-    for (int q = 0; q < kMaxXChunks; q++) {
-        const int i = tid + q * kThreads;
-        if (i < nxc) {
-            const uint2 w = xraw[q];
-            auto cvt2 = [](uint32_t v, int sh) {
-                return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> sh) & 0xFF)) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> (sh + 8)) & 0xFF)) << 16);
-            };
-            const int word = 4 * i;  // logical word of this chunk (token m = word / (K/2))
-            const int m = word / (int)(K / 2), wk = word - m * (int)(K / 2);
-            const int d = wk & 127, lj = d >> 4, c = (d >> 2) & 3;
-            const int phys = m * xtok + (wk >> 7) * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2);
-            *reinterpret_cast<uint4 *>(xs + phys) = make_uint4(cvt2(w.x, 0), cvt2(w.x, 16), cvt2(w.y, 0), cvt2(w.y, 16));
+        for (int m = 0; m < MT; m++) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kFusedBlocks; i++) {
+                if (wave64 + 16 * i < nblk) {
+                    fwht256_lane4(xr[m][i], lane64);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(xr[m][i][q]));
+                }
+            }
+#pragma unroll
+            for (int sh = 32; sh > 0; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+            if (lane64 == 0) red[m * (kThreads / 64) + wave64] = amax;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            float amax = red[m * (kThreads / 64)];
+#pragma unroll
+            for (int w = 1; w < kThreads / 64; w++) amax = fmaxf(amax, red[m * (kThreads / 64) + w]);
+            const float sxm = amax / 127.0f;
+            sx_all[m] = sxm;
+            if (blockIdx.x == 0 && tid == 0) a.s_x_out[m] = sxm;
+#pragma unroll
+            for (int i = 0; i < kFusedBlocks; i++) {
+                const int b = wave64 + 16 * i;
+                if (b < nblk) {
+                    const uint32_t q4 = (amax > 0.0f) ? quant4(xr[m][i], sxm) : 0u;
+                    if (blockIdx.x == 0)
+                        reinterpret_cast<uint32_t *>(a.x_q_out + m * K)[(b * kRot) / 4 + lane64] = q4;
+                    const int lj = lane64 >> 3, c = (lane64 >> 1) & 3;
+                    const int phys = m * xtok + b * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2) + 2 * (lane64 & 1);
+                    *reinterpret_cast<uint2 *>(xs + phys) = make_uint2(cvt2(q4, 0), cvt2(q4, 16));
+                }
+            }
         }
     }
     __syncthreads();
@@ -302,7 +367,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
         for (int t = 0; t < nblk; t++) acc += pp[t];
         const float sch = (i < kThreads && m == 0) ? sch_mine : a.s_ch[r0 + rl];
         const int64_t r = r0 + rl;
-        const float v = ((acc * sch) * a.s_x[m]) * cbscale;
+        float sxm = sx_all[0];
+#pragma unroll
+        for (int q = 1; q < MT; q++) sxm = (m == q) ? sx_all[q] : sxm;
+        const float v = ((acc * sch) * sxm) * cbscale;
         if (a.y_bf16)
             static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(v);
         else
@@ -310,10 +378,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     }
 }
 
-template <int MT>
+template <int MT, int XIN>
 hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
     const int64_t nblk = a.K / kRot;
-    const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4;  // dynamic part; the 64 KiB table is static
+    // dynamic part (the 64 KiB table is static): activations, then a [MT][16] scratch for
+    // the fused preparation's wave maxima, then the partials
+    const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4 + (XIN ? (int64_t)MT * (kThreads / 64) * 4 : 0);
     int64_t rows = (a.N + num_cu - 1) / num_cu;
     rows += rows & 1;
     const int64_t dyn_max = kLdsMax - (int64_t)kTabWords * 4;
@@ -323,14 +393,14 @@ hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
     if (lds > dyn_max) return hipErrorInvalidValue;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kLdsMax - kTabWords * 4));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const unsigned grid = (unsigned)((a.N + rows - 1) / rows);
-    hipLaunchKernelGGL(k_gemv<MT>, dim3(grid), dim3(kThreads), (size_t)lds, stream, a, (int)rows);
+    hipLaunchKernelGGL((k_gemv<MT, XIN>), dim3(grid), dim3(kThreads), (size_t)lds, stream, a, (int)rows);
     return hipGetLastError();
 }
 
@@ -338,14 +408,24 @@ hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
 
 bool gemv_supported(int64_t M, int64_t K) { return M >= 1 && M <= kMaxMT && M * K <= 40960; }
 
+bool gemv_fused_supported(int64_t M, int64_t K) {
+    return M >= 1 && M <= 2 && K <= (int64_t)16 * kFusedBlocks * kRot;
+}
+
 hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream) {
     switch (a.M) {
-        case 1: return launch_mt<1>(a, num_cu, stream);
-        case 2: return launch_mt<2>(a, num_cu, stream);
-        case 3: return launch_mt<3>(a, num_cu, stream);
-        case 4: return launch_mt<4>(a, num_cu, stream);
+        case 1: return launch_mt<1, 0>(a, num_cu, stream);
+        case 2: return launch_mt<2, 0>(a, num_cu, stream);
+        case 3: return launch_mt<3, 0>(a, num_cu, stream);
+        case 4: return launch_mt<4, 0>(a, num_cu, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream) {
+    if (a.M == 1) return a.x_bf16 ? launch_mt<1, 2>(a, num_cu, stream) : launch_mt<1, 1>(a, num_cu, stream);
+    if (a.M == 2) return a.x_bf16 ? launch_mt<2, 2>(a, num_cu, stream) : launch_mt<2, 1>(a, num_cu, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace w4a8

@@ -25,31 +25,6 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRegBlocks = 5;
 
 template <bool BF16>
-__device__ __forceinline__ void load4(const void *x, int64_t off, float v[4]) {
-    if constexpr (BF16) {
-        uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + off);
-        v[0] = __uint_as_float(u.x << 16);
-        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(u.y << 16);
-        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    } else {
-        float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    }
-}
-
-__device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
-    uint32_t out = 0;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        float r = rintf(v[q] / s);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        out |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * q);
-    }
-    return out;
-}
-
-template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_prepare(const void *__restrict__ x, int64_t K,
                                                       int8_t *__restrict__ xq,
                                                       float *__restrict__ sx) {

@@ -55,20 +55,6 @@ WsLayout layout(int64_t N, int64_t K) {
     return L;
 }
 
-template <bool BF16>
-__device__ __forceinline__ void load4w(const void *w, int64_t off, float v[4]) {
-    if constexpr (BF16) {
-        uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(w) + off);
-        v[0] = __uint_as_float(u.x << 16);
-        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        v[2] = __uint_as_float(u.y << 16);
-        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    } else {
-        float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(w) + off);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    }
-}
-
 // Group scale, normalised values and the s_rel byte of one 16-group spread over 4 lanes.
 __device__ __forceinline__ void scale_block(float v[4], float rmax, int lane, float *vout,
                                             uint8_t *srel_out) {
@@ -104,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void k_rotate_scale(const void *__restric
         for (int i = 0; i < kRegBlocks; i++) {
             const int b = wave + i * kWaves;
             if (b < nblk) {
-                load4w<BF16>(w, row + (int64_t)b * kRot + 4 * lane, keep[i]);
+                load4<BF16>(w, row + (int64_t)b * kRot + 4 * lane, keep[i]);
                 fwht256_lane4(keep[i], lane);
 #pragma unroll
                 for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(keep[i][q]));
@@ -113,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void k_rotate_scale(const void *__restric
     } else {
         for (int b = wave; b < nblk; b += kWaves) {
             float v[4];
-            load4w<BF16>(w, row + (int64_t)b * kRot + 4 * lane, v);
+            load4<BF16>(w, row + (int64_t)b * kRot + 4 * lane, v);
             fwht256_lane4(v, lane);
 #pragma unroll
             for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(v[q]));
@@ -137,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_rotate_scale(const void *__restric
     } else {
         for (int b = wave; b < nblk; b += kWaves) {
             float v[4];
-            load4w<BF16>(w, row + (int64_t)b * kRot + 4 * lane, v);
+            load4<BF16>(w, row + (int64_t)b * kRot + 4 * lane, v);
             fwht256_lane4(v, lane);
             scale_block(v, rmax, lane, vout + row + (int64_t)b * kRot, srow + b * 16);
         }

@@ -71,6 +71,34 @@ __device__ __forceinline__ void fwht256_lane4(float v[4], int lane) {
     for (int q = 0; q < 4; q++) v[q] = v[q] * 0.0625f;
 }
 
+// Four consecutive activations (fp32, or bf16 widened exactly) starting at element off.
+template <bool BF16>
+__device__ __forceinline__ void load4(const void *x, int64_t off, float v[4]) {
+    if constexpr (BF16) {
+        uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + off);
+        v[0] = __uint_as_float(u.x << 16);
+        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(u.y << 16);
+        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+        float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+}
+
+// Per-token symmetric int8 of four rotated values with scale s = amax / 127 (s > 0): IEEE
+// division, round to nearest even, clamp to +-127; packed little-endian into one word.
+__device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        float r = rintf(v[q] / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        out |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * q);
+    }
+    return out;
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -97,10 +125,17 @@ struct LinearArgs {
     const float *cb;
     void *y;
     int y_bf16;
+    // fused activation preparation (w4a8_forward): raw activations in, x_q / s_x out
+    const void *x_raw;
+    int x_bf16;
+    int8_t *x_q_out;
+    float *s_x_out;
 };
 
 bool gemv_supported(int64_t M, int64_t K);
+bool gemv_fused_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream);
+hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream);
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
 
