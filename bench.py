@@ -227,18 +227,20 @@ def main():
         for (n, k) in shapes:
             xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
             y = torch.empty((M, n), dtype=torch.float32, device="cuda")
-            for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"),):
+            for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16")):
                 g = make_graph(torch, lambda: [w.linear(xq, sx, pl[(n, k)][c], out=y, algo=algo)
                                                for c in range(2)])
                 t = time_graph_launches(torch, g, 2, 10)
                 tops = 2.0 * M * n * k / t / 1e12
-                pre[f"{n}x{k}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
+                pre[f"{n}x{k}/{name}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
                 log(f"prefill {name} M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
-        tops_all = [v["tops"] for v in pre.values()]
-        out["prefill"] = dict(tokens=M, shapes=pre, tops=round(float(np.mean(tops_all)), 1),
-                              roofline=dict(bound="mfma", achieved=round(float(np.mean(tops_all)), 1),
-                                            peak=INT8_PEAK_TOPS, unit="TOP/s",
-                                            frac=round(float(np.mean(tops_all)) / INT8_PEAK_TOPS, 4)))
+        summary = {}
+        for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s")):
+            vals = [v["tops"] for v in pre.values() if v["algo"] == name]
+            mean = float(np.mean(vals))
+            summary[name] = dict(tops=round(mean, 1), roofline=dict(
+                bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
+        out["prefill"] = dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
 
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(shapes)
     print(json.dumps(out), flush=True)

@@ -214,15 +214,32 @@ def test_mfma_i8_full_size_sampled(w, N, K):
     i8_tight(y, q, xq, sx, rows, toks)
 
 
-@pytest.mark.parametrize("algo", ["gemv", "mfma_i8"])
+@pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (512, 256, 257),
+                                   (17, 5120, 3)])
+def test_mfma_f16_parity(w, N, K, M):
+    say(f"mfma_f16 N={N} K={K} M={M}")
+    y, yr, A, _ = run_linear(w, w.ALGO_MFMA_F16, N, K, M, n_out=2)
+    assert_gate(y, yr, A)
+
+
+@pytest.mark.parametrize("N,K", [S.MLP_GATE_UP, S.MLP_DOWN])
+def test_mfma_f16_full_size_sampled(w, N, K):
+    M = 2048
+    say(f"mfma_f16 full N={N} K={K} M={M}")
+    rows, toks = sample(N, 384, N), sample(M, 48, M + 1)
+    y, yr, A, _ = run_linear(w, w.ALGO_MFMA_F16, N, K, M, rows=rows, toks=toks)
+    assert_gate(y, yr, A)
+
+
+@pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16"])
 def test_bf16_output(w, algo):
-    a = {"gemv": 1, "mfma_i8": 2}[algo]
+    a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3}[algo]
     say(f"bf16 output {algo}")
     y, yr, A, _ = run_linear(w, a, 256, 512, 2, out_dtype=torch.bfloat16, n_out=2)
     assert_gate(y, yr, A, extra=2.0 ** -8 * np.abs(yr))
 
 
-@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (0, 1), (0, 300)])
+@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (0, 1), (0, 300)])
 def test_deterministic_and_auto(w, algo, M):
     say(f"determinism algo={algo} M={M}")
     N, K = 512, 1024

@@ -122,7 +122,8 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     int st = check_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype);
     if (st != W4A8_OK) return st;
     if (algo == W4A8_ALGO_AUTO) algo = pick(M, K);
-    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8) return W4A8_ERR_DTYPE;
+    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8 && algo != W4A8_ALGO_MFMA_F16)
+        return W4A8_ERR_DTYPE;
     if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
     int num_cu = 0;
     st = current_device(&num_cu);
@@ -133,7 +134,8 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     hipError_t e;
     switch (algo) {
         case W4A8_ALGO_GEMV: e = w4a8::launch_gemv(a, num_cu, s); break;
-        default: e = w4a8::launch_gemm_i8(a, s); break;
+        case W4A8_ALGO_MFMA_I8: e = w4a8::launch_gemm_i8(a, s); break;
+        default: e = w4a8::launch_gemm_f16(a, s); break;
     }
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }

@@ -27,6 +27,9 @@ typedef int int16v __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 128, BN = 128, BK = 64;
 constexpr int kThreads = 256;
+// Padded LDS row strides: 72 B per activation row and 36 B per packed row put the 32 rows
+// that one fragment read touches on distinct banks (LDS has 32 four-byte banks).
+constexpr int kXRow = BK + 8, kPRow = BK / 2 + 4;
 
 struct CbI8 {
     uint32_t t[4];  // cb_i8[0..15] as bytes
@@ -55,8 +58,8 @@ __device__ __forceinline__ uint2 slot_order(uint32_t d0, uint32_t d1) {
 }
 
 __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
-    __shared__ __align__(16) uint8_t xs[2][BM * BK];
-    __shared__ __align__(16) uint8_t ps[2][BN * BK / 2];
+    __shared__ __align__(16) uint8_t xs[2][BM * kXRow];
+    __shared__ __align__(16) uint8_t ps[2][BN * kPRow];
     __shared__ __align__(16) uint8_t ss[2][BN * BK / kGroup];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -91,10 +94,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
     const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(a.s_rel + (svalid ? (n0 + tid) * (K / kGroup) : 0));
     const uint32_t xmask = xvalid ? 0xFFFFFFFFu : 0u, pmask = pvalid ? 0xFFFFFFFFu : 0u;
     const uint32_t smask = svalid ? 0xFFFFFFFFu : 0u;
-    uint8_t *xdst0 = &xs[0][xr * BK + 32 * xh];
-    uint8_t *pdst0 = &ps[0][pr * (BK / 2) + 16 * ph];
+    uint8_t *xdst0 = &xs[0][xr * kXRow + 32 * xh];
+    uint8_t *pdst0 = &ps[0][pr * kPRow + 16 * ph];
     uint8_t *sdst0 = &ss[0][(tid & (BN - 1)) * 4];
-    constexpr int xbuf = BM * BK, pbuf = BN * BK / 2, sbuf = BN * BK / kGroup;
+    constexpr int xbuf = BM * kXRow, pbuf = BN * kPRow, sbuf = BN * BK / kGroup;
 
     float acc[2][2][16];
 #pragma unroll
@@ -113,11 +116,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
         const uint2 o1 = slot_order(rx0.z & xmask, rx0.w & xmask);                              \
         const uint2 o2 = slot_order(rx1.x & xmask, rx1.y & xmask);                              \
         const uint2 o3 = slot_order(rx1.z & xmask, rx1.w & xmask);                              \
-        uint4 *dx = reinterpret_cast<uint4 *>(xdst0 + (buf) * xbuf);                            \
-        dx[0] = make_uint4(o0.x, o0.y, o1.x, o1.y);                                             \
-        dx[1] = make_uint4(o2.x, o2.y, o3.x, o3.y);                                             \
-        *reinterpret_cast<uint4 *>(pdst0 + (buf) * pbuf) =                                       \
-            make_uint4(rp.x & pmask, rp.y & pmask, rp.z & pmask, rp.w & pmask);                  \
+        uint2 *dx = reinterpret_cast<uint2 *>(xdst0 + (buf) * xbuf);  /* 8-B aligned rows */   \
+        dx[0] = o0; dx[1] = o1; dx[2] = o2; dx[3] = o3;                                         \
+        uint32_t *dp = reinterpret_cast<uint32_t *>(pdst0 + (buf) * pbuf); /* 4-B aligned */    \
+        dp[0] = rp.x & pmask; dp[1] = rp.y & pmask; dp[2] = rp.z & pmask; dp[3] = rp.w & pmask;  \
         if (tid < BN) *reinterpret_cast<uint32_t *>(sdst0 + (buf) * sbuf) = rs & smask;          \
     } while (0)
     W4A8_STAGE_STORE(0);
@@ -141,12 +143,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
 #pragma unroll
             for (int ib = 0; ib < 2; ib++) {
                 const int row = wm * 64 + ib * 32 + l32;
-                A[ib] = *reinterpret_cast<const long *>(&xs[buf][row * BK + g * kGroup + 8 * half]);
+                A[ib] = *reinterpret_cast<const long *>(&xs[buf][row * kXRow + g * kGroup + 8 * half]);
             }
 #pragma unroll
             for (int jb = 0; jb < 2; jb++) {
                 const int row = wn * 64 + jb * 32 + l32;
-                const uint32_t w = *reinterpret_cast<const uint32_t *>(&ps[buf][row * (BK / 2) + g * 8 + 4 * half]);
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(&ps[buf][row * kPRow + g * 8 + 4 * half]);
                 B[jb] = decode8(cbt, w);
                 s[jb] = e4m3_to_f32(ss[buf][row * 4 + g]);
             }
