@@ -2,26 +2,39 @@
 
 Headline (one JSON line on stdout): effective weight GB/s of the decode hot path at M=1.
 One step = the whole per-call path for one token on the two MLP shapes of a 27B-class
-decoder -- prepare_activation + linear for gate/up (N=17408, K=5120) and for down
-(N=5120, K=17408) -- with inputs resident in HBM.  Each shape has 8 distinct weight copies
-(~400 MB per shape, beyond the 256 MB Infinity Cache) and consecutive steps use
-consecutive copies, so every step streams its weights from HBM.  Steps are replayed from
-HIP graphs (8 steps per graph) so host launch cost does not pace the GPU.
+decoder -- Hadamard-256 rotation + per-token int8 quantisation + W4A8 product, for gate/up
+(N=17408, K=5120) and for down (N=5120, K=17408), one fused launch each (w4a8_forward) --
+with inputs resident in HBM.  Each shape has 8 distinct weight copies (~400 MB per shape,
+beyond the 256 MB Infinity Cache) and consecutive steps use consecutive copies, so every
+step streams its weights from HBM.  Steps are replayed from HIP graphs (8 steps per graph)
+so host launch cost does not pace the GPU.
 
 value = weight-side bytes per step (packed + group scales + row scales + codebook of both
 matrices) / measured time per step.  The same line carries:
-  roofline      the decode GEMV kernel: algorithmic bytes per launch / its average launch
-                duration (HIP events around back-to-back launches on the launch stream)
-                against 8 TB/s;
-  prefill       the int8-MFMA GEMM at M=2048 on both shapes: int8 TOPS against 5.0 POPS;
+  roofline      the fused decode kernel k_gemv<1,XIN=1>: algorithmic bytes per launch / its
+                average launch duration (HIP events on the launch stream around the timed
+                region) against 8 TB/s; traffic = HBM bytes per launch from rocprofv3
+                FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration, when the
+                committed counter summary matches the current kernel source (else null);
+  gemv          the same for the prepared-input GEMV kernel (w4a8_linear, M=1);
+  sweep         batched decode: M in {1,2,4,8,16,32,64} x four projection shapes, every
+                kernel that supports the point, plus the automatic choice (prepare included);
+  model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
+                token = 248 fused forwards + 248 prepared-input linears from one HIP graph;
+  prefill       M=2048 GEMMs on both MLP shapes: int8-MFMA (per-16 fold) and f16-MFMA;
   cpu_baseline  the CPU oracle (prepare + fp64 product) on the same M=1 workload, timed on
                 this host's cores.
+
+--pmc-pass runs each kernel a few times eagerly (plus a plain copy of known size for
+calibration) and prints nothing else: it is the program profiled by the counter runs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,6 +48,11 @@ INT8_PEAK_TOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
 COPIES = 8
 METRIC = "W4A8 linear: effective weight GB/s (M=1) + int8 TOPS (M=2048) on 1 MI355X"
+SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
+MODEL_LAYERS = 62
+CALIB_BYTES = 1 << 30  # the copy kernel of the counter calibration reads and writes 1 GiB
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemv_fused_m1_mlp_traffic.md")
+GEMV_SOURCES = ("w4a8_codebook_gemm_amd/csrc/k_gemv.hip", "w4a8_codebook_gemm_amd/csrc/w4a8_internal.h")
 
 
 def log(*a):
@@ -46,8 +64,35 @@ def weight_bytes(n, k):
 
 
 def gemv_bytes(n, k, m=1):
-    """Algorithmic HBM bytes of one linear launch: weights + x_q + s_x + fp32 y."""
+    """Algorithmic HBM bytes of one prepared-input linear launch: weights + x_q + s_x + fp32 y."""
     return weight_bytes(n, k) + m * k + 4 * m + 4 * m * n
+
+
+def forward_bytes(n, k, m=1):
+    """Algorithmic HBM bytes of one fused forward launch: weights + fp32 x in + x_q, s_x out
+    + fp32 y out."""
+    return weight_bytes(n, k) + 4 * m * k + m * k + 4 * m + 4 * m * n
+
+
+def source_sha256(paths=GEMV_SOURCES):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per fused-forward launch from the committed counter summary, or None when it
+    is missing or was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch=(\d+)\s+source_sha256=([0-9a-f]{64})", text)
+    if not m or m.group(2) != source_sha256():
+        return None
+    return int(m.group(1))
 
 
 def build_layers(w, torch, shapes, copies):
@@ -58,11 +103,14 @@ def build_layers(w, torch, shapes, copies):
         base = w.quantize_weight(W, seed=0)
         torch.cuda.synchronize()
         del W
-        layers[(n, k)] = [w.QuantizedLinear(base.packed.clone(), base.s_rel.clone(),
-                                            base.s_channel.clone(), base.codebook.clone())
-                          for _ in range(copies)]
+        layers[(n, k)] = [clone_layer(w, base) for _ in range(copies)]
         torch.cuda.synchronize()
     return layers
+
+
+def clone_layer(w, base):
+    return w.QuantizedLinear(base.packed.clone(), base.s_rel.clone(), base.s_channel.clone(),
+                             base.codebook.clone())
 
 
 def make_graph(torch, fn):
@@ -85,9 +133,9 @@ def busy(torch):
         torch.cuda._sleep(20_000_000)
 
 
-def time_graph_launches(torch, graph, launches_per_replay, replays):
-    """Average GPU time per launch of a graph of back-to-back launches (HIP events on
-    the current stream, the stream the library launches on)."""
+def time_graph(torch, graph, replays):
+    """GPU seconds per replay of a graph (HIP events on the current stream, the stream the
+    graph and the library's kernels run on)."""
     busy(torch)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -95,7 +143,7 @@ def time_graph_launches(torch, graph, launches_per_replay, replays):
         graph.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e-3 / (launches_per_replay * replays)
+    return a.elapsed_time(b) * 1e-3 / replays
 
 
 def cpu_baseline(shapes, target_s=10.0):
@@ -122,6 +170,219 @@ def cpu_baseline(shapes, target_s=10.0):
                        f"shapes 17408x5120 and 5120x17408, {el:.1f} s")
 
 
+def decode(w, torch, S, args, shapes):
+    """The headline: fused decode step over both MLP shapes, plus the per-kernel rooflines."""
+    layers = build_layers(w, torch, shapes, COPIES)
+    xs = {(n, k): torch.from_numpy(S.activations(1, k, seed=0)).cuda() for (n, k) in shapes}
+    xqs = {(n, k): (torch.empty((1, k), dtype=torch.int8, device="cuda"),
+                    torch.empty((1,), dtype=torch.float32, device="cuda")) for (n, k) in shapes}
+    ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
+
+    def step(c):
+        for sh in shapes:
+            w.forward(xs[sh], layers[sh][c], out=ys[sh], x_q=xqs[sh][0], s_x=xqs[sh][1])
+
+    def step_unfused(c):
+        for sh in shapes:
+            w.prepare_activation(xs[sh], out=xqs[sh])
+            w.linear(*xqs[sh], layers[sh][c], out=ys[sh])
+
+    full = make_graph(torch, lambda: [step(c) for c in range(COPIES)])
+    rem = args.steps % COPIES
+    tail = make_graph(torch, lambda: [step(c) for c in range(rem)]) if rem else None
+
+    def run(nsteps):
+        for _ in range(nsteps // COPIES):
+            full.replay()
+        if nsteps % COPIES:
+            tail.replay()
+
+    warm = args.warmup - args.warmup % COPIES
+    run(warm)
+    torch.cuda.synchronize()
+    busy(torch)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    run(args.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    el = ev0.elapsed_time(ev1) * 1e-3
+    ms_step = el * 1e3 / args.steps
+    wb = sum(weight_bytes(n, k) for (n, k) in shapes)
+    value = wb / (el / args.steps) / 1e9
+    log(f"decode step: {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth "
+        f"(host wall clock incl. the busy-wait kernel {wall:.3f} s)")
+
+    # the dominant kernel is the fused forward: 2 launches per step, back to back
+    t_fwd = el / (2 * args.steps)
+    per_fwd = sum(forward_bytes(n, k) for (n, k) in shapes) / len(shapes)
+    ach = per_fwd / t_fwd / 1e9
+    traffic = measured_traffic()
+    roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="k_gemv<1,1> (fused rotate + quantise + W4A8 GEMV, fp32 x)",
+                    per_launch_bytes=int(per_fwd), avg_launch_us=round(t_fwd * 1e6, 3))
+    log(f"fused forward: {t_fwd * 1e6:.2f} us per launch, {ach:.1f} GB/s algorithmic, "
+        f"traffic {traffic}")
+
+    reps = max(4, args.steps // (4 * COPIES))
+    unf = make_graph(torch, lambda: [step_unfused(c) for c in range(COPIES)])
+    t_unf = time_graph(torch, unf, reps) / COPIES
+    log(f"decode step with separate prepare launches: {t_unf * 1e6:.2f} us")
+
+    for sh in shapes:
+        w.prepare_activation(xs[sh], out=xqs[sh])
+    torch.cuda.synchronize()
+    gemv_g = make_graph(torch, lambda: [w.linear(*xqs[sh], layers[sh][c], out=ys[sh], algo=w.ALGO_GEMV)
+                                        for c in range(COPIES) for sh in shapes])
+    t_gemv = time_graph(torch, gemv_g, reps) / (COPIES * len(shapes))
+    per_gemv = sum(gemv_bytes(n, k) for (n, k) in shapes) / len(shapes)
+    log(f"GEMV (prepared x_q): {t_gemv * 1e6:.2f} us per launch, {per_gemv / t_gemv / 1e9:.1f} GB/s")
+    gemv = dict(kernel="k_gemv<1,0> (prepared int8 x)", avg_launch_us=round(t_gemv * 1e6, 3),
+                per_launch_bytes=int(per_gemv), achieved=round(per_gemv / t_gemv / 1e9, 1),
+                frac=round(per_gemv / t_gemv / 1e9 / HBM_PEAK_GBS, 4))
+    out = dict(value=value, ms_step=ms_step, warm=warm, wb=wb, roofline=roofline, gemv=gemv,
+               unfused_step_us=round(t_unf * 1e6, 2), tokens_per_s=round(1.0 / (el / args.steps), 1))
+    del layers
+    return out
+
+
+def sweep(w, torch, S):
+    """Batched decode: every kernel that supports (M, shape), and the automatic choice."""
+    shapes = [S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE, S.ATTN_WIDE]
+    layers = build_layers(w, torch, shapes, COPIES)
+    algos = (("gemv", w.ALGO_GEMV), ("mfma_i8", w.ALGO_MFMA_I8), ("mfma_f16", w.ALGO_MFMA_F16))
+    res = {}
+    for (n, k) in shapes:
+        for m in SWEEP_M:
+            x = torch.from_numpy(S.activations(m, k, seed=0)).cuda()
+            xq, sx = w.prepare_activation(x)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            point = {}
+            for name, algo in algos:
+                try:  # the warm call (before capture) rejects points outside a kernel's range
+                    g = make_graph(torch, lambda: [w.linear(xq, sx, layers[(n, k)][c], out=y, algo=algo)
+                                                   for c in range(COPIES)])
+                except w.W4A8Error as e:
+                    if e.status != 2:
+                        raise
+                    continue
+                point[name] = round(time_graph(torch, g, 8) / COPIES * 1e6, 2)
+            g = make_graph(torch, lambda: [w.forward(x, layers[(n, k)][c], out=y, x_q=xq, s_x=sx)
+                                           for c in range(COPIES)])
+            t_auto = time_graph(torch, g, 8) / COPIES
+            best = min(point, key=point.get)
+            tb = point[best] * 1e-6
+            res[f"{n}x{k}/M={m}"] = dict(
+                us=point, best=best, auto=w.linear_pick(m, n, k), auto_forward_us=round(t_auto * 1e6, 2),
+                weight_gbs=round(weight_bytes(n, k) / tb / 1e9, 1), tokens_per_s=round(m / tb, 1),
+                tops=round(2.0 * m * n * k / tb / 1e12, 2))
+            log(f"sweep {n}x{k} M={m}: {point} auto(forward) {t_auto * 1e6:.2f} us")
+    del layers
+    return res
+
+
+def model(w, torch, S, tokens=20):
+    """62 layers x (gate, up 17408x5120; down 5120x17408; five 5120x5120): one token reads every
+    weight once.  Inputs per layer: the attention input feeds four square projections, the
+    attention output the fifth; the MLP input feeds gate and up; the MLP hidden feeds down.
+    The first projection of each input runs the fused forward (it writes x_q, s_x), the others
+    reuse x_q through w4a8_linear."""
+    base = {}
+    for sh in (S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE):
+        W = torch.from_numpy(S.weights(*sh, seed=0)).cuda()
+        base[sh] = w.quantize_weight(W, seed=0)
+        torch.cuda.synchronize()
+        del W
+    layers = []
+    for _ in range(MODEL_LAYERS):
+        layers.append(dict(attn=[clone_layer(w, base[S.ATTN_SQUARE]) for _ in range(5)],
+                           gate=clone_layer(w, base[S.MLP_GATE_UP]), up=clone_layer(w, base[S.MLP_GATE_UP]),
+                           down=clone_layer(w, base[S.MLP_DOWN])))
+    torch.cuda.synchronize()
+    total = sum(weight_bytes(*t) for t in [S.ATTN_SQUARE] * 5 + [S.MLP_GATE_UP] * 2 + [S.MLP_DOWN]) * MODEL_LAYERS
+    d, f = S.ATTN_SQUARE[1], S.MLP_DOWN[1]
+    xs = {key: torch.from_numpy(S.activations(1, k, seed=i)).cuda()
+          for i, (key, k) in enumerate((("attn_in", d), ("attn_out", d), ("mlp_in", d), ("mlp_hid", f)))}
+    xq = {key: (torch.empty((1, v.shape[1]), dtype=torch.int8, device="cuda"),
+                torch.empty((1,), dtype=torch.float32, device="cuda")) for key, v in xs.items()}
+    y5, y17 = (torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (d, S.MLP_GATE_UP[0]))
+
+    def token():
+        for L in layers:
+            w.forward(xs["attn_in"], L["attn"][0], out=y5, x_q=xq["attn_in"][0], s_x=xq["attn_in"][1])
+            for j in (1, 2, 3):
+                w.linear(*xq["attn_in"], L["attn"][j], out=y5)
+            w.forward(xs["attn_out"], L["attn"][4], out=y5, x_q=xq["attn_out"][0], s_x=xq["attn_out"][1])
+            w.forward(xs["mlp_in"], L["gate"], out=y17, x_q=xq["mlp_in"][0], s_x=xq["mlp_in"][1])
+            w.linear(*xq["mlp_in"], L["up"], out=y17)
+            w.forward(xs["mlp_hid"], L["down"], out=y5, x_q=xq["mlp_hid"][0], s_x=xq["mlp_hid"][1])
+
+    g = make_graph(torch, token)
+    g.replay()
+    torch.cuda.synchronize()
+    t = time_graph(torch, g, tokens)
+    log(f"model: {MODEL_LAYERS} layers, {total / 1e9:.2f} GB, {t * 1e3:.3f} ms/token, "
+        f"{1 / t:.1f} tokens/s, {total / t / 1e9:.1f} GB/s")
+    out = dict(layers=MODEL_LAYERS, projections_per_layer=8, launches_per_token=8 * MODEL_LAYERS,
+               weight_bytes=total, ms_per_token=round(t * 1e3, 4), tokens_per_s=round(1 / t, 1),
+               weight_gbs=round(total / t / 1e9, 1), hbm_bound_tokens_per_s=round(HBM_PEAK_GBS * 1e9 / total, 1))
+    del layers, base, g
+    return out
+
+
+def prefill(w, torch, S, shapes, M=2048):
+    pl = build_layers(w, torch, shapes, 2)
+    pre = {}
+    for (n, k) in shapes:
+        xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
+        y = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16")):
+            g = make_graph(torch, lambda: [w.linear(xq, sx, pl[(n, k)][c], out=y, algo=algo) for c in range(2)])
+            t = time_graph(torch, g, 10) / 2
+            tops = 2.0 * M * n * k / t / 1e12
+            pre[f"{n}x{k}/{name}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
+            log(f"prefill {name} M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
+    summary = {}
+    for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s")):
+        mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
+        summary[name] = dict(tops=round(mean, 1), roofline=dict(
+            bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
+    del pl
+    return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
+
+
+def pmc_pass(w, torch, S, shapes):
+    """Eager launches for the counter runs: a plain elementwise copy of CALIB_BYTES (reads and
+    writes that many bytes once) for calibration, then the fused forward and the prepared-input
+    GEMV on every weight copy, then the two prefill GEMMs."""
+    a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    layers = build_layers(w, torch, shapes, COPIES)
+    for sh in shapes:
+        x = torch.from_numpy(S.activations(1, sh[1], seed=0)).cuda()
+        xq, sx = w.prepare_activation(x)
+        y = torch.empty((1, sh[0]), dtype=torch.float32, device="cuda")
+        for c in range(COPIES):
+            w.forward(x, layers[sh][c], out=y, x_q=xq, s_x=sx)
+        for c in range(COPIES):
+            w.linear(xq, sx, layers[sh][c], out=y, algo=w.ALGO_GEMV)
+    torch.cuda.synchronize()
+    for (n, k) in shapes:
+        xq, sx = w.prepare_activation(torch.from_numpy(S.activations(2048, k, seed=0)).cuda())
+        y = torch.empty((2048, n), dtype=torch.float32, device="cuda")
+        for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16):
+            w.linear(xq, sx, layers[(n, k)][0], out=y, algo=algo)
+    torch.cuda.synchronize()
+    log("pmc pass done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +390,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=80)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-model", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -142,106 +406,35 @@ def main():
     torch.cuda.set_device(0)
     w.lib()
     shapes = [S.MLP_GATE_UP, S.MLP_DOWN]
-    layers = build_layers(w, torch, shapes, COPIES)
-    xs = {(n, k): torch.from_numpy(S.activations(1, k, seed=0)).cuda() for (n, k) in shapes}
-    xqs = {(n, k): (torch.empty((1, k), dtype=torch.int8, device="cuda"),
-                    torch.empty((1,), dtype=torch.float32, device="cuda")) for (n, k) in shapes}
-    ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
+    if args.pmc_pass:
+        pmc_pass(w, torch, S, shapes)
+        return
 
-    def step(c):
-        """The decode hot path for one token on both shapes: rotation + int8 quantisation +
-        W4A8 product, fused into one launch per matrix."""
-        for sh in shapes:
-            w.forward(xs[sh], layers[sh][c], out=ys[sh], x_q=xqs[sh][0], s_x=xqs[sh][1])
-
-    def step_unfused(c):
-        for sh in shapes:
-            w.prepare_activation(xs[sh], out=xqs[sh])
-            w.linear(*xqs[sh], layers[sh][c], out=ys[sh])
-
-    def step_graph(cs, fn=step):
-        return make_graph(torch, lambda: [fn(c) for c in cs])
-
-    full = step_graph(range(COPIES))
-    rem = args.steps % COPIES
-    tail = step_graph(range(rem)) if rem else None
-
-    def run(nsteps):
-        for _ in range(nsteps // COPIES):
-            full.replay()
-        if nsteps % COPIES:
-            assert nsteps % COPIES == rem
-            tail.replay()
-
-    warm = args.warmup - args.warmup % COPIES
-    run(warm)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run(args.steps)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms_step = el * 1e3 / args.steps
-    wb = sum(weight_bytes(n, k) for (n, k) in shapes)
-    value = wb / (el / args.steps) / 1e9
-    log(f"decode step: {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth")
-    unf = step_graph(range(COPIES), step_unfused)
-    t_unf = time_graph_launches(torch, unf, COPIES, max(4, args.steps // (4 * COPIES)))
-    log(f"decode step with separate prepare launches: {t_unf * 1e6:.2f} us")
-
-    # the dominant kernel: decode GEMV, back-to-back launches over the 16 distinct matrices
-    for sh in shapes:
-        w.prepare_activation(xs[sh], out=xqs[sh])
-    torch.cuda.synchronize()
-    gemv_g = make_graph(torch, lambda: [w.linear(*xqs[sh], layers[sh][c], out=ys[sh], algo=w.ALGO_GEMV)
-                                        for c in range(COPIES) for sh in shapes])
-    launches = COPIES * len(shapes)
-    t_gemv = time_graph_launches(torch, gemv_g, launches, max(4, args.steps // (4 * COPIES)))
-    per_launch = sum(gemv_bytes(n, k) for (n, k) in shapes) / len(shapes)
-    achieved = per_launch / t_gemv / 1e9
-    log(f"GEMV: {t_gemv * 1e6:.2f} us per launch (mean of both shapes), {achieved:.1f} GB/s")
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="k_gemv<1>", per_launch_bytes=int(per_launch),
-                    avg_launch_us=round(t_gemv * 1e6, 3))
-
+    d = decode(w, torch, S, args, shapes)
+    torch.cuda.empty_cache()
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": warm, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": round(d["value"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": d["warm"], "ms_per_step": round(d["ms_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "decode M=1: rotate + int8-quantise + W4A8 product (w4a8_forward), "
                                "gate/up 17408x5120 and down 5120x17408, "
                                f"{COPIES} distinct weight copies per shape",
-                   "tokens": 1, "weight_bytes_per_step": wb},
-        "tokens_per_s": round(1.0 / (el / args.steps), 1),
-        "unfused_step_us": round(t_unf * 1e6, 2),
-        "roofline": roofline,
+                   "tokens": 1, "weight_bytes_per_step": d["wb"]},
+        "tokens_per_s": d["tokens_per_s"],
+        "unfused_step_us": d["unfused_step_us"],
+        "roofline": d["roofline"],
+        "gemv": d["gemv"],
     }
-
-    if not args.no_prefill:
-        M = 2048
-        del layers
+    if not args.no_sweep:
+        out["sweep"] = sweep(w, torch, S)
         torch.cuda.empty_cache()
-        pl = build_layers(w, torch, shapes, 2)
-        pre = {}
-        for (n, k) in shapes:
-            xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
-            y = torch.empty((M, n), dtype=torch.float32, device="cuda")
-            for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16")):
-                g = make_graph(torch, lambda: [w.linear(xq, sx, pl[(n, k)][c], out=y, algo=algo)
-                                               for c in range(2)])
-                t = time_graph_launches(torch, g, 2, 10)
-                tops = 2.0 * M * n * k / t / 1e12
-                pre[f"{n}x{k}/{name}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
-                log(f"prefill {name} M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
-        summary = {}
-        for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s")):
-            vals = [v["tops"] for v in pre.values() if v["algo"] == name]
-            mean = float(np.mean(vals))
-            summary[name] = dict(tops=round(mean, 1), roofline=dict(
-                bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
-        out["prefill"] = dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
-
+    if not args.no_model:
+        out["model"] = model(w, torch, S)
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
+        out["prefill"] = prefill(w, torch, S, shapes)
+        torch.cuda.empty_cache()
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(shapes)
     print(json.dumps(out), flush=True)
 
