@@ -151,8 +151,9 @@ W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, in
 /*
  * Activation preparation and product in one call: the same results as
  * w4a8_prepare_activation(x -> x_q, s_x) followed by w4a8_linear(x_q, s_x -> y), bit for
- * bit in x_q and s_x and within the same bound in y.  For decode sizes (M <= 2 and
- * K <= 20480) both run in ONE kernel launch: the GEMV's workgroups rotate and quantise
+ * bit in x_q and s_x and within the same bound in y.  For decode sizes (M = 1 with
+ * K <= 32768, or M = 2 with K <= 20480) both run in ONE kernel launch: the GEMV's
+ * workgroups rotate and quantise
  * the activations in their prologue [card "...w4a8-convrot-ComfyUI", section "Why this
  * exists": every generated token re-reads all weights, so per-token fixed costs matter];
  * otherwise the two steps run as separate launches.  x_q [M][K] and s_x [M] are

@@ -68,8 +68,11 @@ def sample(n, count, seed):
 
 # ----------------------------------------------------------------------------- prepare
 
+# K from one block (one 64-thread workgroup) through two register rounds (K <= 32768) to the
+# two-pass path for longer rows
 PREP_CASES = [(4, 512, "f32"), (4, 512, "bf16"), (1, 256, "f32"), (3, 5120, "f32"),
-              (2, 17408, "bf16"), (37, 768, "f32"), (5, 20736, "f32"), (2048, 5120, "bf16")]
+              (2, 17408, "bf16"), (37, 768, "f32"), (5, 20736, "f32"), (2048, 5120, "bf16"),
+              (3, 32768, "f32"), (3, 33024, "bf16"), (2, 65536, "f32")]
 
 
 @pytest.mark.parametrize("M,K,dt", PREP_CASES)
@@ -269,14 +272,16 @@ def test_end_to_end_layer_call(w):
     assert_gate(y.cpu().numpy().astype(np.float64), yr, A)
 
 
+# fused (M = 1, K <= 32768; M = 2, K <= 20480) and two-launch cases on both sides of each limit
 FWD_CASES = [(256, 512, 1, "f32"), (256, 512, 2, "bf16"), (1001, 768, 1, "bf16"), (64, 20480, 1, "f32"),
-             (8, 20480, 2, "f32"), (300, 256, 2, "f32"), (200, 1024, 7, "f32"), (128, 20736, 1, "bf16")]
+             (8, 20480, 2, "f32"), (300, 256, 2, "f32"), (200, 1024, 7, "f32"), (128, 20736, 1, "bf16"),
+             (64, 32768, 1, "bf16"), (40, 33024, 1, "f32"), (24, 20736, 2, "f32")]
 
 
 @pytest.mark.parametrize("N,K,M,dt", FWD_CASES)
 def test_forward_fused_and_fallback(w, N, K, M, dt):
     """w4a8_forward: x_q and s_x bit-exact with the oracle's preparation, y within the bound
-    (one launch for M <= 2 and K <= 20480, two launches otherwise)."""
+    (one launch for M = 1, K <= 32768 and M = 2, K <= 20480; two launches otherwise)."""
     say(f"forward N={N} K={K} M={M} {dt}")
     _, q = oracle_layer(N, K, 3)
     x = S.activations(M, K, seed=N + K + M, n_outliers=2)

@@ -49,9 +49,9 @@ constexpr int kMaxXChunks = 40960 / 8 / kThreads;  // 8-value activation chunks 
 // Activation words per 256-wide K block in LDS: 128 fp16 pairs + 4 words of padding, so
 // lane groups reading consecutive blocks start on different banks.
 constexpr int kXBlk = 132;
-// Fused activation preparation keeps a token's rotated row in registers: 16 waves x 5
-// blocks of 256, so K <= 20480.
-constexpr int kFusedBlocks = 5;
+// Fused activation preparation keeps a token's rotated row in registers: 64 lane rows of
+// 16 x 2 rounds of 256-blocks, so K <= 32768.
+constexpr int kFusedRounds = 2;
 
 template <int MT>
 constexpr int depth() { return 2; }  // units in flight per 8-lane group (more only adds contention)
@@ -202,8 +202,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
     const int nxc = (int)(MT * (K / 8));
     uint2 xraw[XIN == 0 ? kMaxXChunks : 1];
-    float xr[XIN == 0 ? 1 : MT][kFusedBlocks][4];  // raw activations: wave w holds blocks w + 16 i
+    // raw activations: lane row g16 (16 lanes) holds block g16 + 64 r, 16 values per lane
+    float xr[XIN == 0 ? 1 : MT][kFusedRounds][16];
     const int lane64 = tid & 63, wave64 = tid >> 6;
+    const int g16 = tid >> 4, t16 = tid & 15, h16 = fwht_row16_nibble(t16);
     if constexpr (XIN == 0) {
 #pragma unroll
         for (int m = 0; m < MT; m++) sx_all[m] = a.s_x[m];
@@ -216,9 +218,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
 #pragma unroll
         for (int m = 0; m < MT; m++)
 #pragma unroll
-            for (int i = 0; i < kFusedBlocks; i++) {
-                const int b = wave64 + 16 * i;
-                if (b < nblk) load4<XIN == 2>(a.x_raw, m * K + (int64_t)b * kRot + 4 * lane64, xr[m][i]);
+            for (int r = 0; r < kFusedRounds; r++) {
+                const int b = g16 + 64 * r;
+                if (b < nblk) {
+                    load16<XIN == 2>(a.x_raw, m * K + (int64_t)b * kRot + 16 * h16, xr[m][r]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; q++) xr[m][r][q] = 0.0f;
+                }
             }
     }
 
@@ -281,11 +288,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
         for (int m = 0; m < MT; m++) {
             float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < kFusedBlocks; i++) {
-                if (wave64 + 16 * i < nblk) {
-                    fwht256_lane4(xr[m][i], lane64);
+            for (int r = 0; r < kFusedRounds; r++) {
+                if (64 * r < nblk) {  // uniform: every lane row rotates (zeros past the end)
+                    fwht256_row16(xr[m][r], t16);
 #pragma unroll
-                    for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(xr[m][i][q]));
+                    for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(xr[m][r][q]));
                 }
             }
 #pragma unroll
@@ -302,15 +309,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
             sx_all[m] = sxm;
             if (blockIdx.x == 0 && tid == 0) a.s_x_out[m] = sxm;
 #pragma unroll
-            for (int i = 0; i < kFusedBlocks; i++) {
-                const int b = wave64 + 16 * i;
+            for (int r = 0; r < kFusedRounds; r++) {
+                const int b = g16 + 64 * r;
                 if (b < nblk) {
-                    const uint32_t q4 = (amax > 0.0f) ? quant4(xr[m][i], sxm) : 0u;
+                    const uint4 q16 = (amax > 0.0f) ? quant16(xr[m][r], sxm) : make_uint4(0, 0, 0, 0);
                     if (blockIdx.x == 0)
-                        reinterpret_cast<uint32_t *>(a.x_q_out + m * K)[(b * kRot) / 4 + lane64] = q4;
-                    const int lj = lane64 >> 3, c = (lane64 >> 1) & 3;
-                    const int phys = m * xtok + b * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2) + 2 * (lane64 & 1);
-                    *reinterpret_cast<uint2 *>(xs + phys) = make_uint2(cvt2(q4, 0), cvt2(q4, 16));
+                        reinterpret_cast<uint4 *>(a.x_q_out + m * K)[(b * kRot + 16 * h16) / 16] = q16;
+                    // this lane's 16 values are logical words 8h .. 8h+7 of the block: lane
+                    // slot h >> 1, chunks 2 (h & 1) and 2 (h & 1) + 1
+                    const int lj = h16 >> 1, c0 = 2 * (h16 & 1), sw = (lj >> 1) & 3;
+                    const int base = m * xtok + b * kXBlk + (lj << 4);
+                    *reinterpret_cast<uint4 *>(xs + base + ((c0 ^ sw) << 2)) =
+                        make_uint4(cvt2(q16.x, 0), cvt2(q16.x, 16), cvt2(q16.y, 0), cvt2(q16.y, 16));
+                    *reinterpret_cast<uint4 *>(xs + base + (((c0 + 1) ^ sw) << 2)) =
+                        make_uint4(cvt2(q16.z, 0), cvt2(q16.z, 16), cvt2(q16.w, 0), cvt2(q16.w, 16));
                 }
             }
         }
@@ -409,7 +421,7 @@ hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
 bool gemv_supported(int64_t M, int64_t K) { return M >= 1 && M <= kMaxMT && M * K <= 40960; }
 
 bool gemv_fused_supported(int64_t M, int64_t K) {
-    return M >= 1 && M <= 2 && K <= (int64_t)16 * kFusedBlocks * kRot;
+    return M >= 1 && M <= 2 && K <= (int64_t)64 * kFusedRounds * kRot && gemv_supported(M, K);
 }
 
 hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream) {

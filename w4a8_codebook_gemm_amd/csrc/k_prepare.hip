@@ -8,54 +8,71 @@
 // product equals the original one (the orthonormal Sylvester transform is its own
 // inverse).
 //
-// One workgroup of 16 waves per token row.  A wave owns whole 256-blocks: lane l holds
-// elements 4l..4l+3 of a block in registers, so the transform's spans 1 and 2 are
-// in-lane and spans 4..128 are lane-xor exchanges of distance 1..32.  Every butterfly is
-// one fp32 add and one fp32 subtract in the fixed stage order 1, 2, 4, ..., 128, then the
-// exact x 1/16: the int8 result is bit-reproducible.  Rows of up to 16 waves x 5 blocks
-// (K <= 20480) stay in registers between the amax reduction and the quantisation;
-// longer rows are rotated twice (identical arithmetic) instead of being stored.
+// One workgroup per token row.  Each 256-block belongs to one 16-lane DPP row (16
+// consecutive values per lane, see fwht256_row16): the rotation needs no LDS, and a lane's
+// 16 results are 16 consecutive int8 outputs (one 16-byte store).  The workgroup is sized to
+// the row (16 lanes per block, at most 1024 threads); every block's loads are issued before
+// the first rotation so their latencies overlap.  Rows of up to two blocks per lane group
+// (K <= 32768) stay in registers between the amax reduction and the quantisation; longer
+// rows are rotated twice (identical arithmetic) instead of being stored.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRegBlocks = 5;
+constexpr int kMaxThreads = 1024;
+constexpr int kRegRounds = 2;
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_prepare(const void *__restrict__ x, int64_t K,
-                                                      int8_t *__restrict__ xq,
-                                                      float *__restrict__ sx) {
-    __shared__ float red[kWaves];
+__global__ __launch_bounds__(kMaxThreads) void k_prepare(const void *__restrict__ x, int64_t K,
+                                                         int8_t *__restrict__ xq,
+                                                         float *__restrict__ sx) {
+    __shared__ float red[kMaxThreads / 64];
     const int64_t m = blockIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    const int groups = blockDim.x >> 4;           // 16-lane rows, one 256-block each per round
+    const int g = tid >> 4, t = tid & 15;
+    const int h = fwht_row16_nibble(t);
     const int nblk = (int)(K / kRot);
+    const int rounds = (nblk + groups - 1) / groups;
     const int64_t row = m * K;
-    const bool in_regs = nblk <= kWaves * kRegBlocks;
+    const bool in_regs = rounds <= kRegRounds;
 
-    float keep[kRegBlocks][4];
+    float keep[kRegRounds][16];
     float amax = 0.0f;
     if (in_regs) {
 #pragma unroll
-        for (int i = 0; i < kRegBlocks; i++) {
-            const int b = wave + i * kWaves;
+        for (int r = 0; r < kRegRounds; r++) {
+            const int b = g + r * groups;
             if (b < nblk) {
-                load4<BF16>(x, row + (int64_t)b * kRot + 4 * lane, keep[i]);
-                fwht256_lane4(keep[i], lane);
+                load16<BF16>(x, row + (int64_t)b * kRot + 16 * h, keep[r]);
+            } else {
 #pragma unroll
-                for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(keep[i][q]));
+                for (int q = 0; q < 16; q++) keep[r][q] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kRegRounds; r++) {
+            if (r < rounds) {  // uniform over the workgroup
+                fwht256_row16(keep[r], t);
+#pragma unroll
+                for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(keep[r][q]));
             }
         }
     } else {
-        for (int b = wave; b < nblk; b += kWaves) {
-            float v[4];
-            load4<BF16>(x, row + (int64_t)b * kRot + 4 * lane, v);
-            fwht256_lane4(v, lane);
+        for (int r = 0; r < rounds; r++) {
+            const int b = g + r * groups;
+            float v[16];
+            if (b < nblk) {
+                load16<BF16>(x, row + (int64_t)b * kRot + 16 * h, v);
+            } else {
 #pragma unroll
-            for (int q = 0; q < 4; q++) amax = fmaxf(amax, fabsf(v[q]));
+                for (int q = 0; q < 16; q++) v[q] = 0.0f;
+            }
+            fwht256_row16(v, t);
+#pragma unroll
+            for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(v[q]));
         }
     }
 #pragma unroll
@@ -63,24 +80,30 @@ __global__ __launch_bounds__(kThreads) void k_prepare(const void *__restrict__ x
     if (lane == 0) red[wave] = amax;
     __syncthreads();
     amax = red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; w++) amax = fmaxf(amax, red[w]);
+    for (int w = 1; w < nwaves; w++) amax = fmaxf(amax, red[w]);
 
     const float s = amax / 127.0f;
-    if (threadIdx.x == 0) sx[m] = s;
-    uint32_t *out = reinterpret_cast<uint32_t *>(xq + row);
+    if (tid == 0) sx[m] = s;
+    uint4 *out = reinterpret_cast<uint4 *>(xq + row);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
     if (in_regs) {
 #pragma unroll
-        for (int i = 0; i < kRegBlocks; i++) {
-            const int b = wave + i * kWaves;
-            if (b < nblk) out[(b * kRot) / 4 + lane] = (amax > 0.0f) ? quant4(keep[i], s) : 0u;
+        for (int r = 0; r < kRegRounds; r++) {
+            const int b = g + r * groups;
+            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16(keep[r], s) : zero;
         }
     } else {
-        for (int b = wave; b < nblk; b += kWaves) {
-            float v[4];
-            load4<BF16>(x, row + (int64_t)b * kRot + 4 * lane, v);
-            fwht256_lane4(v, lane);
-            out[(b * kRot) / 4 + lane] = (amax > 0.0f) ? quant4(v, s) : 0u;
+        for (int r = 0; r < rounds; r++) {
+            const int b = g + r * groups;
+            float v[16];
+            if (b < nblk) {
+                load16<BF16>(x, row + (int64_t)b * kRot + 16 * h, v);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; q++) v[q] = 0.0f;
+            }
+            fwht256_row16(v, t);
+            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16(v, s) : zero;
         }
     }
 }
@@ -89,7 +112,10 @@ __global__ __launch_bounds__(kThreads) void k_prepare(const void *__restrict__ x
 
 hipError_t launch_prepare(const void *x, int x_bf16, int64_t M, int64_t K, int8_t *x_q,
                           float *s_x, hipStream_t stream) {
-    dim3 grid((unsigned)M), block(kThreads);
+    // 16 lanes per 256-block, whole waves, at most kMaxThreads
+    const int64_t want = ((K / kRot) * 16 + 63) / 64 * 64;
+    const unsigned threads = (unsigned)(want < kMaxThreads ? want : kMaxThreads);
+    dim3 grid((unsigned)M), block(threads);
     if (x_bf16)
         hipLaunchKernelGGL(k_prepare<true>, grid, block, 0, stream, x, K, x_q, s_x);
     else

@@ -71,6 +71,70 @@ __device__ __forceinline__ void fwht256_lane4(float v[4], int lane) {
     for (int q = 0; q < 4; q++) v[q] = v[q] * 0.0625f;
 }
 
+// The same rotation of one 256-block on the 16 lanes of a DPP row, 16 values per lane, with
+// no LDS traffic.  Element bits 0..3 index the lane's registers (v[j] = element 16h + j), so
+// spans 1..8 are in-lane; element bits 4..7 (the "high nibble" h) are spread over the row's
+// lanes as h = t ^ 3*bit2(t) for row position t.  Under that map, flipping element bit 4, 5,
+// 6 or 7 is lane xor 1, 2, 7 or 8: the DPP patterns quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror and row_ror:8, each a single exchange within the row.  A cross-lane
+// butterfly computes fma(+-1, own, partner): exactly one rounding of (lower + upper) on the
+// lower lane and (lower - upper) on the upper lane, so the result is bit-identical to the
+// add/subtract order above.  Every lane of the row must execute it.
+__device__ __forceinline__ int fwht_row16_nibble(int t) { return t ^ (((t >> 2) & 1) * 3); }
+
+template <int CTRL>
+__device__ __forceinline__ void fwht_row16_stage(float v[16], float sgn) {
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+        const float p = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(v[q]), CTRL, 0xF, 0xF, false));
+        v[q] = fmaf(sgn, v[q], p);
+    }
+}
+
+__device__ __forceinline__ void fwht256_row16(float v[16], int t) {
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            if (i & s) continue;
+            const float a = v[i], b = v[i + s];
+            v[i] = a + b;
+            v[i + s] = a - b;
+        }
+    }
+    const int h = fwht_row16_nibble(t);
+    fwht_row16_stage<0xB1>(v, (h & 1) ? -1.0f : 1.0f);   // span 16:  lane ^ 1
+    fwht_row16_stage<0x4E>(v, (h & 2) ? -1.0f : 1.0f);   // span 32:  lane ^ 2
+    fwht_row16_stage<0x141>(v, (h & 4) ? -1.0f : 1.0f);  // span 64:  lane ^ 7 (half mirror)
+    fwht_row16_stage<0x128>(v, (h & 8) ? -1.0f : 1.0f);  // span 128: lane ^ 8 (rotate by 8)
+#pragma unroll
+    for (int q = 0; q < 16; q++) v[q] = v[q] * 0.0625f;
+}
+
+// Sixteen consecutive activations (fp32, or bf16 widened exactly) starting at element off
+// (a multiple of 16).
+template <bool BF16>
+__device__ __forceinline__ void load16(const void *x, int64_t off, float v[16]) {
+    if constexpr (BF16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = p[i];
+            v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+        }
+    }
+}
+
 // Four consecutive activations (fp32, or bf16 widened exactly) starting at element off.
 template <bool BF16>
 __device__ __forceinline__ void load4(const void *x, int64_t off, float v[4]) {
@@ -97,6 +161,11 @@ __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
         out |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * q);
     }
     return out;
+}
+
+// quant4 over sixteen values -> sixteen int8 bytes.
+__device__ __forceinline__ uint4 quant16(const float v[16], float s) {
+    return make_uint4(quant4(v, s), quant4(v + 4, s), quant4(v + 8, s), quant4(v + 12, s));
 }
 
 // ---------------------------------------------------------------- misc
