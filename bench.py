@@ -253,7 +253,8 @@ def sweep(w, torch, S):
     """Batched decode: every kernel that supports (M, shape), and the automatic choice."""
     shapes = [S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE, S.ATTN_WIDE]
     layers = build_layers(w, torch, shapes, COPIES)
-    algos = (("gemv", w.ALGO_GEMV), ("mfma_i8", w.ALGO_MFMA_I8), ("mfma_f16", w.ALGO_MFMA_F16))
+    algos = (("gemv", w.ALGO_GEMV), ("mfma_skinny", w.ALGO_MFMA_SKINNY), ("mfma_i8", w.ALGO_MFMA_I8),
+             ("mfma_f16", w.ALGO_MFMA_F16))
     res = {}
     for (n, k) in shapes:
         for m in SWEEP_M:

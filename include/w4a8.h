@@ -63,11 +63,15 @@ typedef enum { W4A8_F32 = 0, W4A8_BF16 = 1 } w4a8_dtype;
 
 /* Kernel choice for w4a8_linear_algo. */
 typedef enum {
-    W4A8_ALGO_AUTO = 0,     /* pick by M, N, K (what w4a8_linear does) */
-    W4A8_ALGO_GEMV = 1,     /* fp32-codebook streaming GEMV (decode); M <= 4 and M*K <= 40960 */
-    W4A8_ALGO_MFMA_I8 = 2,  /* int8 MFMA on the int8 form of the codebook, exact int32
-                               per-16 partials, fp32 group-scale fold */
-    W4A8_ALGO_MFMA_F16 = 3  /* f16 MFMA on decoded weights (codebook x group scale in f16) */
+    W4A8_ALGO_AUTO = 0,       /* pick by M, N, K (what w4a8_linear does): GEMV for M <= 2
+                                 (within its range), SKINNY for M <= 64, else MFMA_F16 */
+    W4A8_ALGO_GEMV = 1,       /* fp32-codebook streaming GEMV (decode); M <= 4 and M*K <= 40960 */
+    W4A8_ALGO_MFMA_I8 = 2,    /* int8 MFMA on the int8 form of the codebook, exact int32
+                                 per-16 partials, fp32 group-scale fold */
+    W4A8_ALGO_MFMA_F16 = 3,   /* f16 MFMA on decoded weights (codebook x group scale in f16),
+                                 128 x 256 tiles (prefill) */
+    W4A8_ALGO_MFMA_SKINNY = 4 /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
+                                 16-row weight tiles streamed once, M*K < 2^31 */
 } w4a8_algo;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -142,7 +146,8 @@ W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t
                 void *y, int y_dtype, void *stream);
 
 /* As w4a8_linear with an explicit kernel choice (w4a8_algo).  W4A8_ALGO_GEMV returns
- * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960). */
+ * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960), W4A8_ALGO_MFMA_SKINNY outside
+ * its range (M <= 64, M*K < 2^31, 40*K < 2^31). */
 W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,

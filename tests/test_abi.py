@@ -53,7 +53,10 @@ def test_workspace_size_and_pick(L):
         assert L.w4a8_quantize_weight_workspace(*bad) == 0
     assert L.w4a8_linear_pick(1, 17408, 5120) == w.ALGO_GEMV
     assert L.w4a8_linear_pick(2, 5120, 17408) == w.ALGO_GEMV
-    assert L.w4a8_linear_pick(2048, 17408, 5120) == w.ALGO_MFMA_I8
+    assert L.w4a8_linear_pick(3, 17408, 5120) == w.ALGO_MFMA_SKINNY
+    assert L.w4a8_linear_pick(64, 5120, 17408) == w.ALGO_MFMA_SKINNY
+    assert L.w4a8_linear_pick(65, 5120, 17408) == w.ALGO_MFMA_F16
+    assert L.w4a8_linear_pick(2048, 17408, 5120) == w.ALGO_MFMA_F16
     assert L.w4a8_linear_pick(1, 1, 4304) == -2
 
 
@@ -74,6 +77,8 @@ def test_linear_validation(L):
     for k in ("xq", "sx", "pk", "sr", "sc", "cb", "y"):
         assert lin(L, ptrs={k: MIS}) == 4
     assert lin(L, M=8, K=5120, algo=w.ALGO_GEMV) == 2  # outside the GEMV's range
+    assert lin(L, M=65, K=512, algo=w.ALGO_MFMA_SKINNY) == 2  # outside the skinny kernel's
+    assert lin(L, algo=5) == 3
     assert L.w4a8_linear(0, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == 1
 
 

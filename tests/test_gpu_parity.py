@@ -234,15 +234,37 @@ def test_mfma_f16_full_size_sampled(w, N, K):
     assert_gate(y, yr, A)
 
 
-@pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16"])
+# (N, K, M): 16-row tiles per workgroup 1..5 (N = 2048, 5120, 10000, 15360, 17408 on 256 CUs),
+# token tiles 1..4, ragged N and M, K = 256 (waves with no K range)
+SKINNY_CASES = [(256, 512, 3), (300, 768, 17), (1001, 1024, 33), (17, 5120, 64), (64, 256, 5),
+                (2048, 1280, 48), (5120, 768, 16), (10000, 256, 40), (15360, 256, 2), (17408, 256, 8)]
+
+
+@pytest.mark.parametrize("N,K,M", SKINNY_CASES)
+def test_mfma_skinny_parity(w, N, K, M):
+    say(f"mfma_skinny N={N} K={K} M={M}")
+    y, yr, A, _ = run_linear(w, w.ALGO_MFMA_SKINNY, N, K, M, n_out=2)
+    assert_gate(y, yr, A)
+
+
+@pytest.mark.parametrize("N,K,M", [(17408, 5120, 64), (5120, 17408, 16), (15360, 5120, 33), (5120, 5120, 64)])
+def test_mfma_skinny_full_size_sampled(w, N, K, M):
+    say(f"mfma_skinny full N={N} K={K} M={M}")
+    rows = sample(N, 512, N + M)
+    y, yr, A, _ = run_linear(w, w.ALGO_MFMA_SKINNY, N, K, M, rows=rows)
+    assert_gate(y, yr, A)
+
+
+@pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16", "mfma_skinny"])
 def test_bf16_output(w, algo):
-    a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3}[algo]
+    a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3, "mfma_skinny": 4}[algo]
     say(f"bf16 output {algo}")
     y, yr, A, _ = run_linear(w, a, 256, 512, 2, out_dtype=torch.bfloat16, n_out=2)
     assert_gate(y, yr, A, extra=2.0 ** -8 * np.abs(yr))
 
 
-@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (0, 1), (0, 300)])
+@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (4, 3), (4, 64), (0, 1), (0, 8),
+                                    (0, 300)])
 def test_deterministic_and_auto(w, algo, M):
     say(f"determinism algo={algo} M={M}")
     N, K = 512, 1024

@@ -49,9 +49,10 @@ int check_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, cons
     return W4A8_OK;
 }
 
-int pick(int64_t M, int64_t K) {
+int pick(int64_t M, int64_t N, int64_t K) {
     if (w4a8::gemv_supported(M, K) && M <= 2) return W4A8_ALGO_GEMV;
-    return W4A8_ALGO_MFMA_I8;
+    if (w4a8::skinny_supported(M, N, K)) return W4A8_ALGO_MFMA_SKINNY;
+    return W4A8_ALGO_MFMA_F16;
 }
 
 }  // namespace
@@ -112,7 +113,7 @@ int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int64_t K, in
 
 int w4a8_linear_pick(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || !valid_k(K)) return -W4A8_ERR_SHAPE;
-    return pick(M, K);
+    return pick(M, N, K);
 }
 
 int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
@@ -121,10 +122,12 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      void *stream) {
     int st = check_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype);
     if (st != W4A8_OK) return st;
-    if (algo == W4A8_ALGO_AUTO) algo = pick(M, K);
-    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8 && algo != W4A8_ALGO_MFMA_F16)
+    if (algo == W4A8_ALGO_AUTO) algo = pick(M, N, K);
+    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8 && algo != W4A8_ALGO_MFMA_F16 &&
+        algo != W4A8_ALGO_MFMA_SKINNY)
         return W4A8_ERR_DTYPE;
     if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
+    if (algo == W4A8_ALGO_MFMA_SKINNY && !w4a8::skinny_supported(M, N, K)) return W4A8_ERR_SHAPE;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A8_OK) return st;
@@ -135,6 +138,7 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     switch (algo) {
         case W4A8_ALGO_GEMV: e = w4a8::launch_gemv(a, num_cu, s); break;
         case W4A8_ALGO_MFMA_I8: e = w4a8::launch_gemm_i8(a, s); break;
+        case W4A8_ALGO_MFMA_SKINNY: e = w4a8::launch_gemm_skinny(a, num_cu, s); break;
         default: e = w4a8::launch_gemm_f16(a, s); break;
     }
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
@@ -148,7 +152,7 @@ int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t 
     if (st != W4A8_OK) return st;
     if (!valid_dtype(x_dtype)) return W4A8_ERR_DTYPE;
     if (!aligned16(x)) return W4A8_ERR_ALIGN;
-    if (!(w4a8::gemv_fused_supported(M, K) && pick(M, K) == W4A8_ALGO_GEMV)) {
+    if (!(w4a8::gemv_fused_supported(M, K) && pick(M, N, K) == W4A8_ALGO_GEMV)) {
         st = w4a8_prepare_activation(x, x_dtype, M, K, x_q, s_x, stream);
         if (st != W4A8_OK) return st;
         return w4a8_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype, stream);

@@ -207,6 +207,8 @@ hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream);
 hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream);
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
+bool skinny_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream);
 
 size_t quantize_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint64_t seed,
