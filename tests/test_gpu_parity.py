@@ -96,6 +96,32 @@ def test_prepare_bit_exact(w, M, K, dt):
     assert np.array_equal(xq.cpu().numpy(), xq_ref)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_prepare_tiny_scales(w, fused):
+    """Both quantisation routes: ordinary scales (reciprocal with exact correction) and
+    s_x below 2^-100 (IEEE division), including a token of subnormal values."""
+    say(f"prepare tiny scales fused={fused}")
+    M, K = (2, 512) if fused else (4, 512)
+    x = S.activations(M, K, seed=5, n_outliers=2)
+    x[1] *= np.float32(1e-33)                          # amax ~ 1e-32: s_x < 2^-100
+    if M > 2:
+        x[2] = np.float32(1e-40) * np.sign(x[2])       # subnormal inputs
+        x[3] *= np.float32(3e-29)                      # just above the fast-path limit
+    xq_ref, sx_ref = O.prepare(x)
+    if fused:
+        _, q = oracle_layer(64, K, 1)
+        L = gpu_layer(w, q)
+        x_q = torch.empty((M, K), dtype=torch.int8, device=DEV)
+        s_x = torch.empty((M,), dtype=torch.float32, device=DEV)
+        w.forward(gpu(x), L, x_q=x_q, s_x=s_x)
+        xq, sx = x_q, s_x
+    else:
+        xq, sx = w.prepare_activation(gpu(x))
+    torch.cuda.synchronize()
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+
+
 # ----------------------------------------------------------------------------- quantize
 
 def check_quant(w, W, seed, dtype=torch.float32):

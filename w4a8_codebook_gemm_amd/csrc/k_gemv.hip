@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
             float amax = 0.0f;
 #pragma unroll
             for (int r = 0; r < kFusedRounds; r++) {
-                if (64 * r < nblk) {  // uniform: every lane row rotates (zeros past the end)
+                if (g16 + 64 * r < nblk) {  // whole 16-lane rows: absent blocks skip it
                     fwht256_row16(xr[m][r], t16);
 #pragma unroll
                     for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(xr[m][r][q]));
@@ -306,13 +306,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
 #pragma unroll
             for (int w = 1; w < kThreads / 64; w++) amax = fmaxf(amax, red[m * (kThreads / 64) + w]);
             const float sxm = amax / 127.0f;
+            const float rsm = sxm >= kQuantFastMin ? 1.0f / sxm : 0.0f;
             sx_all[m] = sxm;
             if (blockIdx.x == 0 && tid == 0) a.s_x_out[m] = sxm;
 #pragma unroll
             for (int r = 0; r < kFusedRounds; r++) {
                 const int b = g16 + 64 * r;
                 if (b < nblk) {
-                    const uint4 q16 = (amax > 0.0f) ? quant16(xr[m][r], sxm) : make_uint4(0, 0, 0, 0);
+                    const uint4 q16 = (amax > 0.0f) ? quant16_auto(xr[m][r], sxm, rsm) : make_uint4(0, 0, 0, 0);
                     if (blockIdx.x == 0)
                         reinterpret_cast<uint4 *>(a.x_q_out + m * K)[(b * kRot + 16 * h16) / 16] = q16;
                     // this lane's 16 values are logical words 8h .. 8h+7 of the block: lane

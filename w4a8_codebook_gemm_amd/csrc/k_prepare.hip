@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_prepare(const void *__restrict_
         }
 #pragma unroll
         for (int r = 0; r < kRegRounds; r++) {
-            if (r < rounds) {  // uniform over the workgroup
+            if (g + r * groups < nblk) {  // whole 16-lane rows: absent blocks skip the rotation
                 fwht256_row16(keep[r], t);
 #pragma unroll
                 for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(keep[r][q]));
@@ -83,6 +83,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_prepare(const void *__restrict_
     for (int w = 1; w < nwaves; w++) amax = fmaxf(amax, red[w]);
 
     const float s = amax / 127.0f;
+    const float rs = s >= kQuantFastMin ? 1.0f / s : 0.0f;
     if (tid == 0) sx[m] = s;
     uint4 *out = reinterpret_cast<uint4 *>(xq + row);
     const uint4 zero = make_uint4(0, 0, 0, 0);
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_prepare(const void *__restrict_
 #pragma unroll
         for (int r = 0; r < kRegRounds; r++) {
             const int b = g + r * groups;
-            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16(keep[r], s) : zero;
+            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16_auto(keep[r], s, rs) : zero;
         }
     } else {
         for (int r = 0; r < rounds; r++) {
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_prepare(const void *__restrict_
                 for (int q = 0; q < 16; q++) v[q] = 0.0f;
             }
             fwht256_row16(v, t);
-            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16(v, s) : zero;
+            if (b < nblk) out[(b * kRot + 16 * h) / 16] = (amax > 0.0f) ? quant16_auto(v, s, rs) : zero;
         }
     }
 }

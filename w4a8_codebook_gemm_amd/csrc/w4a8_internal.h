@@ -168,6 +168,34 @@ __device__ __forceinline__ uint4 quant16(const float v[16], float s) {
     return make_uint4(quant4(v, s), quant4(v + 4, s), quant4(v + 8, s), quant4(v + 12, s));
 }
 
+// The same bytes with the IEEE quotient v / s formed from r = RN(1 / s) by Markstein's
+// correction: q0 = RN(v r), e = fma(-q0, s, v) (exact), q = fma(e, r, q0) = RN(v / s)
+// (P. Markstein, "Computation of elementary functions on the IBM RISC System/6000
+// processor", IBM J. Res. Dev. 34(1), 1990).  The theorem needs r correctly rounded and no
+// overflow or underflow in the steps: callers use it for s >= kQuantFastMin only (then
+// |v / s| <= 127 and r < 2^100; quotients that underflow are far below 1/2 and round to 0
+// either way).  Checked against IEEE division around every rounding boundary.
+constexpr float kQuantFastMin = 0x1p-100f;
+__device__ __forceinline__ uint32_t quant4_r(const float v[4], float s, float r) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float q0 = v[q] * r;
+        const float e = fmaf(-q0, s, v[q]);
+        float t = rintf(fmaf(e, r, q0));
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        out |= ((uint32_t)(int32_t)t & 0xFFu) << (8 * q);
+    }
+    return out;
+}
+
+// quant16 choosing the exact fast path when the scale allows it (uniform per token).
+__device__ __forceinline__ uint4 quant16_auto(const float v[16], float s, float r) {
+    if (s >= kQuantFastMin)
+        return make_uint4(quant4_r(v, s, r), quant4_r(v + 4, s, r), quant4_r(v + 8, s, r), quant4_r(v + 12, s, r));
+    return quant16(v, s);
+}
+
 // ---------------------------------------------------------------- misc
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
