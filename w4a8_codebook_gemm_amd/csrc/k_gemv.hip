@@ -25,8 +25,8 @@
 //    consumed); the first loads go out before the table build; the weight stream uses
 //    non-temporal buffer loads with workgroup-relative 32-bit offsets.
 //  * Units run in row-major order, so a wave reads 1 KiB contiguous per row and its group
-//    scales as one 128-B run; the activation blocks in LDS are padded by 4 words and their
-//    chunks XOR-swizzled per lane so that concurrent reads spread over the banks.
+//    scales as one 128-B run; the activation chunks in LDS are XOR-swizzled by lane and by
+//    block parity so that the two groups served together cover all 64 LDS banks.
 //  * Each group's two-element dot products are summed in fp32, scaled by the decoded e4m3
 //    group scale, reduced over the 8 lanes with xor shuffles, and written to an LDS
 //    partial per (row, block) (odd row stride: conflict-free); one thread per row then
@@ -46,9 +46,14 @@ constexpr int kTabWords = 256 * 64;                 // 64 KiB
 constexpr int kLdsMax = 160 * 1024;                 // gfx950 LDS per workgroup
 constexpr int kMaxMT = 4;
 constexpr int kMaxXChunks = 40960 / 8 / kThreads;  // 8-value activation chunks per thread
-// Activation words per 256-wide K block in LDS: 128 fp16 pairs + 4 words of padding, so
-// lane groups reading consecutive blocks start on different banks.
-constexpr int kXBlk = 132;
+// Activation words per 256-wide K block in LDS (128 fp16 pairs, unpadded).  Lane j of a
+// group reads the 16 words 16j .. 16j+15 of its block as four 4-word chunks, chunk c stored
+// at position c ^ ((j >> 1) & 3) ^ (block & 1): the 8 lanes of one group cover 32 of the 64
+// banks and the group on the next block (the other 8 lanes served in the same cycle of a
+// 16-byte read) the other 32.
+constexpr int kXBlk = 128;
+
+__device__ __forceinline__ int xchunk_swizzle(int j, int block) { return ((j >> 1) & 3) ^ (block & 1); }
 // Fused activation preparation keeps a token's rotated row in registers: 64 lane rows of
 // 16 x 2 rounds of 256-blocks, so K <= 32768.
 constexpr int kFusedRounds = 2;
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
                 const int word = 4 * i;  // logical word of this chunk (token m = word / (K/2))
                 const int m = word / (int)(K / 2), wk = word - m * (int)(K / 2);
                 const int d = wk & 127, lj = d >> 4, c = (d >> 2) & 3;
-                const int phys = m * xtok + (wk >> 7) * kXBlk + (lj << 4) + ((c ^ ((lj >> 1) & 3)) << 2);
+                const int phys = m * xtok + (wk >> 7) * kXBlk + (lj << 4) + ((c ^ xchunk_swizzle(lj, wk >> 7)) << 2);
                 *reinterpret_cast<uint4 *>(xs + phys) = make_uint4(cvt2(w.x, 0), cvt2(w.x, 16), cvt2(w.y, 0), cvt2(w.y, 16));
             }
         }
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
                         reinterpret_cast<uint4 *>(a.x_q_out + m * K)[(b * kRot + 16 * h16) / 16] = q16;
                     // this lane's 16 values are logical words 8h .. 8h+7 of the block: lane
                     // slot h >> 1, chunks 2 (h & 1) and 2 (h & 1) + 1
-                    const int lj = h16 >> 1, c0 = 2 * (h16 & 1), sw = (lj >> 1) & 3;
+                    const int lj = h16 >> 1, c0 = 2 * (h16 & 1), sw = xchunk_swizzle(lj, b);
                     const int base = m * xtok + b * kXBlk + (lj << 4);
                     *reinterpret_cast<uint4 *>(xs + base + ((c0 ^ sw) << 2)) =
                         make_uint4(cvt2(q16.x, 0), cvt2(q16.x, 16), cvt2(q16.y, 0), cvt2(q16.y, 16));
@@ -330,15 +335,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     }
     __syncthreads();
 
-    const int xsw = (j >> 1) & 3;
+
     auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb, uint32_t sa, uint32_t sb) {
         const int xbase = sl.xw;
+        const int xsw = xchunk_swizzle(j, xbase >> 7);
         uint32_t xv[MT][16];
 #pragma unroll
         for (int m = 0; m < MT; m++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * xtok + xbase + 4 * (q ^ xsw));
+                const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * xtok + xbase + 4 * (q ^ xsw));  // xbase / 128 = block
                 xv[m][4 * q + 0] = v.x; xv[m][4 * q + 1] = v.y;
                 xv[m][4 * q + 2] = v.z; xv[m][4 * q + 3] = v.w;
             }
