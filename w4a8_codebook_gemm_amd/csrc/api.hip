@@ -50,7 +50,7 @@ int check_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, cons
 }
 
 int pick(int64_t M, int64_t N, int64_t K) {
-    if (w4a8::gemv_supported(M, K) && M <= 2) return W4A8_ALGO_GEMV;
+    if (w4a8::gemv_supported(M, K)) return W4A8_ALGO_GEMV;
     if (w4a8::skinny_supported(M, N, K)) return W4A8_ALGO_MFMA_SKINNY;
     return W4A8_ALGO_MFMA_F16;
 }
