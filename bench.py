@@ -22,6 +22,9 @@ matrices) / measured time per step.  The same line carries:
   model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
                 token = 248 fused forwards + 248 prepared-input linears from one HIP graph;
   prefill       M=2048 GEMMs on both MLP shapes: int8-MFMA (per-16 fold) and f16-MFMA;
+  quantize      offline w4a8_quantize_weight on both MLP shapes from fp32 and bf16 weights
+                (rotation, scales, seeded Lloyd-Max fit on 2^20 samples, assignment, packing):
+                weights per second, including the fit's fixed cost;
   cpu_baseline  the CPU oracle (prepare + fp64 product) on the same M=1 workload, timed on
                 this host's cores.
 
@@ -355,6 +358,28 @@ def prefill(w, torch, S, shapes, M=2048):
     return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
 
 
+def quantize_rate(w, torch, S, shapes, reps=3):
+    """Offline quantisation throughput: each call rotates, fits and packs one whole matrix
+    (the sort and the strictly ordered fp64 prefix sum of the fit are a fixed cost per call)."""
+    res = {}
+    for (n, k) in shapes:
+        W32 = torch.from_numpy(S.weights(n, k, seed=0)).cuda()
+        for name, W in (("f32", W32), ("bf16", W32.to(torch.bfloat16))):
+            ws = torch.empty((w.quantize_weight_workspace(n, k),), dtype=torch.uint8, device="cuda")
+            w.quantize_weight(W, seed=0, workspace=ws)  # warm
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                w.quantize_weight(W, seed=0, workspace=ws)
+            torch.cuda.synchronize()
+            t = (time.perf_counter() - t0) / reps
+            res[f"{n}x{k}/{name}"] = dict(ms=round(t * 1e3, 2), gweights_per_s=round(n * k / t / 1e9, 2),
+                                          input_gbs=round(n * k * W.element_size() / t / 1e9, 1))
+            log(f"quantize {n}x{k} {name}: {t * 1e3:.2f} ms, {n * k / t / 1e9:.2f} G weights/s")
+        del W32
+    return res
+
+
 def pmc_pass(w, torch, S, shapes):
     """Eager launches for the counter runs: a plain elementwise copy of CALIB_BYTES (reads and
     writes that many bytes once) for calibration, then the fused forward and the prepared-input
@@ -393,6 +418,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-model", action="store_true")
+    ap.add_argument("--no-quantize", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -435,6 +461,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         out["prefill"] = prefill(w, torch, S, shapes)
+        torch.cuda.empty_cache()
+    if not args.no_quantize:
+        out["quantize"] = quantize_rate(w, torch, S, shapes)
         torch.cuda.empty_cache()
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(shapes)
     print(json.dumps(out), flush=True)

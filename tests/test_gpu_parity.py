@@ -351,3 +351,19 @@ def test_forward_fused_and_fallback(w, N, K, M, dt):
     assert np.array_equal(x_q.cpu().numpy(), xq_ref)
     yr, A = O.linear_ref(xq_ref, sx_ref, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
     assert_gate(y.cpu().numpy().astype(np.float64), yr, A)
+
+
+def test_safetensors_round_trip_on_gpu(w, tmp_path):
+    """Quantise on the GPU, write the four tensors, read them back onto the GPU: the layer's
+    output is bit-identical to the original's."""
+    from w4a8_codebook_gemm_amd import safetensors_io as io
+    say("safetensors round trip on the GPU")
+    W = gpu(S.weights(300, 1024, seed=9))
+    L = w.quantize_weight(W, seed=9)
+    path = str(tmp_path / "layer.safetensors")
+    io.save_layers(path, {"model.layers.3.mlp.up_proj": L})
+    L2 = io.load_layers(path, device=DEV)["model.layers.3.mlp.up_proj"]
+    x = gpu(S.activations(2, 1024, seed=9))
+    y1, y2 = w.forward(x, L), w.forward(x, L2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
