@@ -47,6 +47,8 @@ def lib():
         L.orc_codebook_i8.argtypes = [P, P, P]
         L.orc_linear_i8_ref.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i64, P, i64,
                                         P, P, P]
+        L.orc_quantize_w8.argtypes = [P, i64, i64, P, P]
+        L.orc_linear_w8_ref.argtypes = [P, P, i64, i64, P, P, i64, P]
         _lib = L
     return _lib
 
@@ -196,3 +198,25 @@ def linear_i8_ref(xq, sx, packed, s_rel, s_ch, cb, rows=None, toks=None, want_p=
                             _p(_c(cb, np.float32)), N, _p(rows), nrow, _p(toks), ntok,
                             _p(y), _p(A), _p(P))
     return (y, A, P) if want_p else (y, A)
+
+
+def quantize_w8(W):
+    """W8A8 comparator weights: rotated rows, per-row int8.  Returns (w_q int8 [N, K], s_w fp32 [N])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    assert K % 256 == 0
+    wq = np.empty((N, K), dtype=np.int8)
+    sw = np.empty((N,), dtype=np.float32)
+    lib().orc_quantize_w8(_p(W), N, K, _p(wq), _p(sw))
+    return wq, sw
+
+
+def linear_w8_ref(xq, sx, wq, sw):
+    """W8A8 comparator product in fp64 (exact integer dot products): y [M, N]."""
+    xq = _c(xq, np.int8)
+    wq = _c(wq, np.int8)
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    lib().orc_linear_w8_ref(_p(xq), _p(_c(sx, np.float32)), M, K, _p(wq), _p(_c(sw, np.float32)), N, _p(y))
+    return y

@@ -432,3 +432,48 @@ void orc_linear_i8_ref(const int8_t *xq, const float *sx, int64_t M, int64_t K,
         }
     }
 }
+
+/* ---------------------------------------------------------------- W8A8 comparator
+ * The INT8 ConvRot format the W4A8 layer is weighed against [card A, "Why this exists": an
+ * INT8 ConvRot build of the same model, about twice the weight bytes].  The cards give no
+ * more detail; the reading taken is the plainest one next to the per-token int8
+ * activations: each weight row takes the same 256-block rotation, then one fp32 scale per row
+ * s_w = max |w_rot| / 127 and codes w_q = clamp(rint(w_rot / s_w), -127, 127) (IEEE
+ * division, ties to even); a zero row gives s_w = 0 and w_q = 0.  No codebook, no groups. */
+void orc_quantize_w8(const float *W, int64_t N, int64_t K, int8_t *wq, float *sw) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < N; r++) {
+        float *t = (float *)malloc((size_t)K * sizeof(float));
+        memcpy(t, W + r * K, (size_t)K * sizeof(float));
+        for (int64_t b = 0; b < K; b += ROT) orc_fwht256(t + b);
+        float rmax = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float a = fabsf(t[k]);
+            if (a > rmax) rmax = a;
+        }
+        const float s = rmax / 127.0f;
+        sw[r] = s;
+        for (int64_t k = 0; k < K; k++) {
+            float q = 0.0f;
+            if (rmax > 0.0f) {
+                q = rintf(t[k] / s);
+                q = q > 127.0f ? 127.0f : (q < -127.0f ? -127.0f : q);
+            }
+            wq[r * K + k] = (int8_t)q;
+        }
+        free(t);
+    }
+}
+
+/* y[m][r] = s_x[m] s_w[r] sum_k x_q[m][k] w_q[r][k] in fp64; the integer sum is exact. */
+void orc_linear_w8_ref(const int8_t *xq, const float *sx, int64_t M, int64_t K, const int8_t *wq,
+                       const float *sw, int64_t N, double *y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < N; r++) {
+        for (int64_t m = 0; m < M; m++) {
+            int64_t dot = 0;
+            for (int64_t k = 0; k < K; k++) dot += (int64_t)xq[m * K + k] * (int64_t)wq[r * K + k];
+            y[m * N + r] = (double)sx[m] * (double)sw[r] * (double)dot;
+        }
+    }
+}

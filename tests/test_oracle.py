@@ -446,3 +446,56 @@ def test_plausibility_against_unquantised_product():
     wrel = np.linalg.norm(w_hat - rotate_dense(W)) / np.linalg.norm(W)
     print(f"output rel err {rel:.4f}, weight rel RMS {wrel:.4f}")
     assert rel < 0.15 and wrel < 0.15
+
+
+# ----------------------------------------------------------------------------- W8A8 comparator
+
+def test_w8_quantisation_is_per_row_int8_of_the_rotated_row():
+    """Pinned to the separately pinned activation preparation: a weight row quantises exactly
+    like a token (same rotation, scale and rounding), and to the rounding bound."""
+    W = S.weights(64, 512, seed=21)
+    W[3] = 0.0                                             # zero row
+    wq, sw = O.quantize_w8(W)
+    xq, sx = O.prepare(W)                                  # rows as tokens
+    assert np.array_equal(wq, xq) and np.array_equal(sw.view(np.uint32), sx.view(np.uint32))
+    assert sw[3] == 0 and not wq[3].any()
+    rot = rotate_dense(W)
+    for r in range(64):
+        if sw[r] == 0:
+            continue
+        err = np.abs(rot[r] - sw[r] * wq[r].astype(np.float64))
+        assert err.max() <= sw[r] * (0.5 + 1e-5)
+        assert np.abs(wq[r]).max() == 127
+
+
+def test_w8_product_equals_integer_matmul():
+    W = S.weights(48, 768, seed=22)
+    x = S.activations(3, 768, seed=22, n_outliers=2)
+    wq, sw = O.quantize_w8(W)
+    xq, sx = O.prepare(x)
+    y = O.linear_w8_ref(xq, sx, wq, sw)
+    dot = xq.astype(np.int64) @ wq.astype(np.int64).T      # exact
+    assert np.array_equal(y, sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] * dot)
+    # hand value: one row of all-ones weights against a spike
+    W1 = np.zeros((1, 256), dtype=np.float32)
+    W1[0, 0] = 16.0                                        # rotated row: all entries 1
+    x1 = np.zeros((1, 256), dtype=np.float32)
+    x1[0, 0] = 16.0                                        # rotated token: all entries 1
+    wq1, sw1 = O.quantize_w8(W1)
+    xq1, sx1 = O.prepare(x1)
+    assert (wq1 == 127).all() and (xq1 == 127).all()
+    s32 = float(np.float32(1.0) / np.float32(127.0))        # both scales are the fp32 1/127
+    assert sw1[0] == sx1[0] == np.float32(s32)
+    assert O.linear_w8_ref(xq1, sx1, wq1, sw1)[0, 0] == s32 * s32 * (127 * 127 * 256)
+
+
+def test_w8_plausibility_against_unquantised_product():
+    W = S.weights(256, 512, seed=23)
+    x = S.activations(4, 512, seed=23, n_outliers=2)
+    wq, sw = O.quantize_w8(W)
+    xq, sx = O.prepare(x)
+    y = O.linear_w8_ref(xq, sx, wq, sw)
+    ytrue = x.astype(np.float64) @ W.astype(np.float64).T
+    rel = np.linalg.norm(y - ytrue) / np.linalg.norm(ytrue)
+    print(f"W8A8 output rel err {rel:.4f}")
+    assert rel < 0.05
