@@ -22,6 +22,9 @@ matrices) / measured time per step.  The same line carries:
   model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
                 token = 248 fused forwards + 248 prepared-input linears from one HIP graph;
   prefill       M=2048 GEMMs on both MLP shapes: int8-MFMA (per-16 fold) and f16-MFMA;
+  w8a8          the INT8 ConvRot comparator (same rotation and int8 activations, per-row
+                int8 weights): decode GEMV on both MLP shapes (prepared x_q), a decode step
+                with its prepare launches beside the W4A8 unfused step, and M=2048 GEMMs;
   quantize      offline w4a8_quantize_weight on both MLP shapes from fp32 and bf16 weights
                 (rotation, scales, seeded Lloyd-Max fit on 2^20 samples, assignment, packing):
                 weights per second, including the fit's fixed cost;
@@ -380,6 +383,62 @@ def quantize_rate(w, torch, S, shapes, reps=3):
     return res
 
 
+def w8_gemv_bytes(n, k, m=1):
+    """Algorithmic HBM bytes of one W8A8 linear launch: int8 weights + row scales + x_q + s_x
+    + fp32 y."""
+    return n * k + 4 * n + m * k + 4 * m + 4 * m * n
+
+
+def w8a8(w, torch, S, shapes, w4_gemv, w4_unfused_us, w4_prefill, M=2048):
+    """The comparator on the same workloads: what the halved weight stream buys on MI355X."""
+    layers = {}
+    for (n, k) in shapes:
+        W = torch.from_numpy(S.weights(n, k, seed=0)).cuda()
+        base = w.w8a8_quantize_weight(W)
+        torch.cuda.synchronize()
+        del W
+        layers[(n, k)] = [w.W8Linear(base.w_q.clone(), base.s_w.clone()) for _ in range(COPIES)]
+    torch.cuda.synchronize()
+    xs = {(n, k): torch.from_numpy(S.activations(1, k, seed=0)).cuda() for (n, k) in shapes}
+    xqs = {sh: w.prepare_activation(xs[sh]) for sh in shapes}
+    ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
+    g = make_graph(torch, lambda: [w.w8a8_linear(*xqs[sh], layers[sh][c], out=ys[sh], algo=w.ALGO_GEMV)
+                                   for c in range(COPIES) for sh in shapes])
+    t_gemv = time_graph(torch, g, 25) / (COPIES * len(shapes))
+    per = sum(w8_gemv_bytes(n, k) for (n, k) in shapes) / len(shapes)
+
+    def step(c):
+        for sh in shapes:
+            w.prepare_activation(xs[sh], out=xqs[sh])
+            w.w8a8_linear(*xqs[sh], layers[sh][c], out=ys[sh])
+
+    g = make_graph(torch, lambda: [step(c) for c in range(COPIES)])
+    t_step = time_graph(torch, g, 25) / COPIES
+    log(f"W8A8 GEMV: {t_gemv * 1e6:.2f} us per launch, {per / t_gemv / 1e9:.1f} GB/s; decode step "
+        f"{t_step * 1e6:.2f} us (W4A8 unfused {w4_unfused_us:.2f} us)")
+    out = dict(gemv=dict(kernel="k_w8_gemv<1>", avg_launch_us=round(t_gemv * 1e6, 3), per_launch_bytes=int(per),
+                         achieved=round(per / t_gemv / 1e9, 1), frac=round(per / t_gemv / 1e9 / HBM_PEAK_GBS, 4)),
+               decode_step_us=round(t_step * 1e6, 2), w4a8_unfused_step_us=w4_unfused_us,
+               w4a8_over_w8a8_gemv_time=round(w4_gemv["avg_launch_us"] / (t_gemv * 1e6), 3))
+    pre = {}
+    for (n, k) in shapes:
+        xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
+        y = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        g = make_graph(torch, lambda: [w.w8a8_linear(xq, sx, layers[(n, k)][c], out=y, algo=w.ALGO_MFMA_I8)
+                                       for c in range(2)])
+        t = time_graph(torch, g, 10) / 2
+        tops = 2.0 * M * n * k / t / 1e12
+        pre[f"{n}x{k}"] = dict(us=round(t * 1e6, 1), tops=round(tops, 1))
+        log(f"W8A8 prefill M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
+    mean = float(np.mean([v["tops"] for v in pre.values()]))
+    out["prefill"] = dict(tokens=M, shapes=pre, tops=round(mean, 1), roofline=dict(
+        bound="mfma", achieved=round(mean, 1), peak=INT8_PEAK_TOPS, unit="TOP/s", frac=round(mean / INT8_PEAK_TOPS, 4)))
+    if w4_prefill:
+        out["prefill"]["w4a8_best_tops"] = max(w4_prefill["mfma_i8"]["tops"], w4_prefill["mfma_f16"]["tops"])
+    del layers
+    return out
+
+
 def pmc_pass(w, torch, S, shapes):
     """Eager launches for the counter runs: a plain elementwise copy of CALIB_BYTES (reads and
     writes that many bytes once) for calibration, then the fused forward and the prepared-input
@@ -419,6 +478,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-model", action="store_true")
     ap.add_argument("--no-quantize", action="store_true")
+    ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -461,6 +521,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_prefill:
         out["prefill"] = prefill(w, torch, S, shapes)
+        torch.cuda.empty_cache()
+    if not args.no_w8a8:
+        out["w8a8"] = w8a8(w, torch, S, shapes, d["gemv"], d["unfused_step_us"], out.get("prefill"))
         torch.cuda.empty_cache()
     if not args.no_quantize:
         out["quantize"] = quantize_rate(w, torch, S, shapes)

@@ -172,6 +172,36 @@ W4A8_API int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, cons
  * status if the shape is invalid.  Launches nothing. */
 W4A8_API int w4a8_linear_pick(int64_t M, int64_t N, int64_t K);
 
+/*
+ * W8A8 comparator: the "INT8 ConvRot" build the W4A8 format is weighed against [card
+ * "...w4a8-convrot-ComfyUI", section "Why this exists": an INT8 ConvRot build of the model
+ * takes about twice the weight bytes, and W4A8 runs on the same int8 GEMM path plus a
+ * codebook dequantisation step].  Same rotation and int8 activations as above; the weights
+ * are int8 with one fp32 scale per row and no codebook or group scales.  The pages fix no
+ * more than that; the per-row scale is the plainest reading beside the per-token one.
+ *
+ * Weight quantisation: each row of w [N][K] (element type w_dtype) is rotated and quantised
+ * exactly as w4a8_prepare_activation treats a token: s_w[r] = max |w_rot[r]| / 127 and
+ * w_q[r][k] = clamp(rint(w_rot[r][k] / s_w[r]), -127, 127); a zero row gives 0.
+ *  w_q [N][K] int8, s_w [N] fp32: outputs.   N >= 1; 256 <= K <= 131072, K % 256 == 0.
+ */
+W4A8_API int w4a8_w8a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, int8_t *w_q,
+                                       float *s_w, void *stream);
+
+/*
+ * W8A8 product: y[m][r] = (fp32(sum_k x_q[m][k] * w_q[r][k]) * s_w[r]) * s_x[m], the integer
+ * sum exact in int32 and each product one fp32 rounding, so |y - y_exact| <= 4 * 2^-24 *
+ * |y_exact| (bf16 output adds its own rounding).  Deterministic.
+ *
+ *  x_q, s_x   prepared activations [M][K], [M];  w_q, s_w  [N][K], [N] (as quantised above)
+ *  y          [M][N], element type y_dtype;  M, N >= 1; 256 <= K <= 131072, K % 256 == 0
+ *  algo       W4A8_ALGO_AUTO (GEMV when M <= 4 and M*K <= 65536, else MFMA_I8),
+ *             W4A8_ALGO_GEMV (W4A8_ERR_SHAPE outside that range) or W4A8_ALGO_MFMA_I8 (int8
+ *             MFMA GEMM, any M); any other code is W4A8_ERR_DTYPE.
+ */
+W4A8_API int w4a8_w8a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *w_q,
+                              const float *s_w, int64_t N, void *y, int y_dtype, int algo, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 9 and set(names) == set(w.EXPORTS)
+    assert len(names) == 11 and set(names) == set(w.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 
@@ -126,3 +126,29 @@ def test_forward_validation(L):
     assert f(*args(xdt=4)) == 3
     assert f(*args(x=MIS)) == 4
     assert f(*args(xq=MIS)) == 4
+
+
+def test_w8a8_validation(L):
+    q = L.w4a8_w8a8_quantize_weight
+    assert q(0, 0, 8, 256, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 8, 4304, FAKE, FAKE, None) == 2
+    assert q(FAKE, 0, 8, 131072 + 256, FAKE, FAKE, None) == 2   # exact int32 sums need K <= 2^17
+    assert q(FAKE, 0, 0, 256, FAKE, FAKE, None) == 2
+    assert q(FAKE, 2, 8, 256, FAKE, FAKE, None) == 3
+    assert q(FAKE, 0, 8, 256, MIS, FAKE, None) == 4
+
+    def lin8(M=4, K=512, N=256, ydt=0, algo=0, **ptrs):
+        p = dict(xq=FAKE, sx=FAKE, wq=FAKE, sw=FAKE, y=FAKE)
+        p.update(ptrs)
+        return L.w4a8_w8a8_linear(p["xq"], p["sx"], M, K, p["wq"], p["sw"], N, p["y"], ydt, algo, None)
+
+    for k in ("xq", "sx", "wq", "sw", "y"):
+        assert lin8(**{k: 0}) == 1
+        assert lin8(**{k: MIS}) == 4
+    for M, K, N in [(0, 512, 4), (4, 300, 4), (4, 512, 0), (4, 131072 + 256, 4)]:
+        assert lin8(M=M, K=K, N=N) == 2
+    assert lin8(ydt=2) == 3
+    assert lin8(algo=w.ALGO_MFMA_F16) == 3
+    assert lin8(algo=w.ALGO_MFMA_SKINNY) == 3
+    assert lin8(M=5, algo=w.ALGO_GEMV) == 2              # GEMV: M <= 4
+    assert lin8(M=4, K=16640, algo=w.ALGO_GEMV) == 2     # GEMV: M*K <= 65536

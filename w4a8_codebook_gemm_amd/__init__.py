@@ -28,7 +28,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN"
           5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
            "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
-           "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward")
+           "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward", "w4a8_w8a8_quantize_weight",
+           "w4a8_w8a8_linear")
 
 
 class W4A8Error(RuntimeError):
@@ -66,6 +67,10 @@ def lib():
         L.w4a8_linear_pick.restype = i32
         L.w4a8_forward.argtypes = [P, i32, i64, i64, P, P, P, P, i64, P, i32, P, P, P]
         L.w4a8_forward.restype = i32
+        L.w4a8_w8a8_quantize_weight.argtypes = [P, i32, i64, i64, P, P, P]
+        L.w4a8_w8a8_quantize_weight.restype = i32
+        L.w4a8_w8a8_linear.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, P]
+        L.w4a8_w8a8_linear.restype = i32
         _lib = L
     return _lib
 
@@ -215,3 +220,42 @@ def forward(x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32, ou
 
 def linear_pick(m: int, n: int, k: int) -> int:
     return int(lib().w4a8_linear_pick(m, n, k))
+
+
+# ----------------------------------------------------------------------------- W8A8 comparator
+
+@dataclass
+class W8Linear:
+    """The int8-weight comparator layer: w_q int8 [N, K] (rotated rows), s_w fp32 [N]."""
+    w_q: torch.Tensor
+    s_w: torch.Tensor
+
+
+def w8a8_quantize_weight(w: torch.Tensor) -> W8Linear:
+    """Quantise a [N, K] fp32/bf16 weight to per-row int8 of its rotated rows."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    wp = _dev(w, "w", (torch.float32, torch.bfloat16))
+    w_q = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    s_w = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check(lib().w4a8_w8a8_quantize_weight(wp, _fdtype(w), n, k, w_q.data_ptr(), s_w.data_ptr(), _stream()),
+           "w4a8_w8a8_quantize_weight")
+    return W8Linear(w_q, s_w)
+
+
+def w8a8_linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: W8Linear, out_dtype=torch.float32,
+                algo: int = ALGO_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y [M, N] of the W8A8 comparator (algo: ALGO_AUTO, ALGO_GEMV or ALGO_MFMA_I8)."""
+    m, k = x_q.shape
+    n = layer.w_q.shape[0]
+    if tuple(layer.w_q.shape) != (n, k) or tuple(layer.s_w.shape) != (n,) or tuple(s_x.shape) != (m,):
+        raise ValueError(f"inconsistent shapes: x_q {tuple(x_q.shape)}, s_x {tuple(s_x.shape)}, "
+                         f"w_q {tuple(layer.w_q.shape)}, s_w {tuple(layer.s_w.shape)}")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x_q.device)
+    _check(lib().w4a8_w8a8_linear(_dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
+                                  _dev(layer.w_q, "w_q", (torch.int8,)), _dev(layer.s_w, "s_w", (torch.float32,)),
+                                  n, _dev(out, "y", (torch.float32, torch.bfloat16)), _fdtype(out), algo,
+                                  _stream()), "w4a8_w8a8_linear")
+    return out

@@ -166,6 +166,43 @@ int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t 
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 
+int w4a8_w8a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, int8_t *w_q,
+                              float *s_w, void *stream) {
+    if (!w || !w_q || !s_w) return W4A8_ERR_NULL;
+    if (N < 1 || !valid_k(K) || K > w4a8::kW8MaxK || N > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
+    if (!valid_dtype(w_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(w_q) || !aligned16(s_w)) return W4A8_ERR_ALIGN;
+    int st = current_device(nullptr);
+    if (st != W4A8_OK) return st;
+    // a weight row is quantised exactly as a token is: rotate, per-row max / 127, round
+    hipError_t e = w4a8::launch_prepare(w, w_dtype == W4A8_BF16, N, K, w_q, s_w,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_w8a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *w_q,
+                     const float *s_w, int64_t N, void *y, int y_dtype, int algo, void *stream) {
+    if (!x_q || !s_x || !w_q || !s_w || !y) return W4A8_ERR_NULL;
+    if (M < 1 || N < 1 || !valid_k(K) || K > w4a8::kW8MaxK || M > (int64_t(1) << 31) - 1 ||
+        N > (int64_t(1) << 31) - 1)
+        return W4A8_ERR_SHAPE;
+    if (!valid_dtype(y_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(x_q) || !aligned16(s_x) || !aligned16(w_q) || !aligned16(s_w) || !aligned16(y))
+        return W4A8_ERR_ALIGN;
+    if (algo == W4A8_ALGO_AUTO) algo = w4a8::w8_gemv_supported(M, K) ? W4A8_ALGO_GEMV : W4A8_ALGO_MFMA_I8;
+    if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8) return W4A8_ERR_DTYPE;
+    if (algo == W4A8_ALGO_GEMV && !w4a8::w8_gemv_supported(M, K)) return W4A8_ERR_SHAPE;
+    if (algo == W4A8_ALGO_MFMA_I8 && ((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+        return W4A8_ERR_SHAPE;
+    int num_cu = 0;
+    int st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    w4a8::W8Args a{x_q, s_x, M, K, N, w_q, s_w, y, y_dtype == W4A8_BF16};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = algo == W4A8_ALGO_GEMV ? w4a8::launch_w8_gemv(a, num_cu, s) : w4a8::launch_w8_gemm(a, s);
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
 int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
                 const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
                 void *y, int y_dtype, void *stream) {

@@ -1,0 +1,288 @@
+// Comparator: the W8A8 ("INT8 ConvRot") linear layer the W4A8 format is weighed against.
+//
+// Model card "Qwen3.8-27B-uncensored-w4a8-convrot-ComfyUI", section "Why this exists": an
+// INT8 ConvRot build of the same model takes about twice the weight bytes, and W4A8 runs on
+// the same int8 GEMM path with a codebook dequantisation step added, so its only gain is
+// the smaller weight stream.  The comparator keeps everything of the W4A8 layer except the
+// weight format: the same 256-block Hadamard rotation and per-token int8 activations, and
+// int8 weights w_q [N][K] with one fp32 scale per row (the rotated row's max |w| / 127).
+//
+//   y[m][r] = (fp32(sum_k x_q[m][k] * w_q[r][k]) * s_w[r]) * s_x[m]
+//
+// The integer sums are exact in int32 (|sum| <= 127^2 K < 2^31 for K <= 131072), so only
+// the three fp32 roundings of the epilogue separate y from the exact value.
+//
+// Kernel W1 (decode, M <= 4): a persistent streaming GEMV.  Each workgroup owns an even
+// share of the rows and stages all M activation rows in LDS; each wave walks a contiguous
+// run of 1 KB row chunks (one 16-byte load per lane: eight whole 128-byte lines per load
+// instruction), two batches of four chunks in flight, four v_dot4_i32_i8 per chunk and
+// token.  A wave folds its lane sums with a butterfly when it leaves a row and adds them to
+// the row's int32 accumulator in LDS (integer adds: the result does not depend on order).
+//
+// Kernel W2 (prefill): int8 MFMA GEMM, v_mfma_i32_32x32x32_i8, 128 x 128 tiles per
+// 256-thread workgroup (2 x 2 waves of 64 x 64), 128-byte K stages double-buffered through
+// LDS, int32 accumulation over all of K, scales applied once in the epilogue.  Tiles are
+// numbered so that each XCD works through a contiguous run of them, token tiles fastest,
+// which keeps a weight tile's reuse within one XCD's L2.
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+namespace {
+
+// ---------------------------------------------------------------- W1: decode GEMV
+constexpr int kGvThreads = 1024, kGvWaves = kGvThreads / 64;
+constexpr int kChunk = 1024;        // row bytes covered by one 16-byte load per lane
+constexpr int kDepth = 4;           // chunks per batch of loads (two batches in flight)
+constexpr int kGvMaxRows = 2048;    // rows per workgroup (int32 accumulators in LDS)
+
+template <int MT>
+__device__ __forceinline__ void fetch_batch(uint4 (&w)[kDepth], const int8_t *wrow, int64_t K,
+                                            int &lrow, int &lc, int KC, int u, int u1, int kb_lane) {
+#pragma unroll
+    for (int d = 0; d < kDepth; d++) {
+        const int kb = lc * kChunk + kb_lane;
+        if (u + d < u1 && kb < K)
+            w[d] = *reinterpret_cast<const uint4 *>(wrow + (int64_t)lrow * K + kb);
+        else
+            w[d] = make_uint4(0u, 0u, 0u, 0u);
+        if (++lc == KC) {
+            lc = 0;
+            lrow++;
+        }
+    }
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+template <int MT>
+__device__ __forceinline__ void consume_batch(const uint4 (&w)[kDepth], const int8_t *xs, int64_t K,
+                                              int &crow, int &cc, int KC, int u, int u1, int kb_lane,
+                                              int (&acc)[MT], bool &pending, int *accs, int lane) {
+#pragma unroll
+    for (int d = 0; d < kDepth; d++) {
+        if (u + d >= u1) break;
+        int kx = cc * kChunk + kb_lane;
+        if (kx > K - 16) kx = (int)K - 16;   // lanes past the row end hold zero weights
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(xs + (int64_t)m * K + kx);
+            int s = acc[m];
+            s = __builtin_amdgcn_sdot4((int)w[d].x, (int)x.x, s, false);
+            s = __builtin_amdgcn_sdot4((int)w[d].y, (int)x.y, s, false);
+            s = __builtin_amdgcn_sdot4((int)w[d].z, (int)x.z, s, false);
+            s = __builtin_amdgcn_sdot4((int)w[d].w, (int)x.w, s, false);
+            acc[m] = s;
+        }
+        pending = true;
+        if (++cc == KC) {
+#pragma unroll
+            for (int m = 0; m < MT; m++) {
+                const int v = wave_sum(acc[m]);
+                if (lane == 0) atomicAdd(&accs[crow * MT + m], v);
+                acc[m] = 0;
+            }
+            pending = false;
+            cc = 0;
+            crow++;
+        }
+    }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kGvThreads) void k_w8_gemv(W8Args a) {
+    __shared__ __align__(16) int8_t xs[kW8GemvMaxX];
+    __shared__ int accs[kGvMaxRows * MT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t K = a.K, N = a.N;
+    const int64_t r0 = N * blockIdx.x / gridDim.x, r1 = N * (blockIdx.x + 1) / gridDim.x;
+    const int R = (int)(r1 - r0);
+
+    const int64_t nx = (int64_t)MT * K / 16;
+    for (int64_t i = tid; i < nx; i += kGvThreads)
+        reinterpret_cast<uint4 *>(xs)[i] = reinterpret_cast<const uint4 *>(a.x_q)[i];
+    for (int i = tid; i < R * MT; i += kGvThreads) accs[i] = 0;
+    __syncthreads();
+
+    const int KC = (int)((K + kChunk - 1) / kChunk);
+    const int U = R * KC;
+    const int u0 = (int)((int64_t)U * wave / kGvWaves), u1 = (int)((int64_t)U * (wave + 1) / kGvWaves);
+    const int kb_lane = lane * 16;
+    const int8_t *wrow = a.w_q + r0 * K;
+
+    int lrow = u0 / KC, lc = u0 - lrow * KC;   // next chunk to load
+    int crow = lrow, cc = lc;                  // next chunk to consume
+    int acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; m++) acc[m] = 0;
+    bool pending = false;
+
+    uint4 wa[kDepth], wb[kDepth];
+    fetch_batch<MT>(wa, wrow, K, lrow, lc, KC, u0, u1, kb_lane);
+    for (int u = u0; u < u1; u += 2 * kDepth) {
+        fetch_batch<MT>(wb, wrow, K, lrow, lc, KC, u + kDepth, u1, kb_lane);
+        consume_batch<MT>(wa, xs, K, crow, cc, KC, u, u1, kb_lane, acc, pending, accs, lane);
+        fetch_batch<MT>(wa, wrow, K, lrow, lc, KC, u + 2 * kDepth, u1, kb_lane);
+        consume_batch<MT>(wb, xs, K, crow, cc, KC, u + kDepth, u1, kb_lane, acc, pending, accs, lane);
+    }
+    if (pending) {   // the wave's run ended inside a row
+#pragma unroll
+        for (int m = 0; m < MT; m++) {
+            const int v = wave_sum(acc[m]);
+            if (lane == 0) atomicAdd(&accs[crow * MT + m], v);
+        }
+    }
+    __syncthreads();
+
+    for (int i = tid; i < R * MT; i += kGvThreads) {
+        const int m = i / R, row = i - m * R;
+        const int64_t r = r0 + row;
+        const float v = ((float)accs[row * MT + m] * a.s_w[r]) * a.s_x[m];
+        if (a.y_bf16)
+            static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(v);
+        else
+            static_cast<float *>(a.y)[m * N + r] = v;
+    }
+}
+
+// ---------------------------------------------------------------- W2: prefill GEMM
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int16v __attribute__((ext_vector_type(16)));
+
+constexpr int GB = 128;             // tile edge (tokens and weight rows)
+constexpr int GK = 128;             // K bytes per stage
+constexpr int kGmThreads = 256;
+// 144-byte LDS rows: the 16 rows one 16-lane phase of a fragment read touches start at
+// distinct multiples of 16 bytes modulo 256, i.e. on disjoint bank quads of the 64 banks
+constexpr int kPitch = GK + 16;
+
+__global__ __launch_bounds__(kGmThreads) void k_w8_gemm(W8Args a, int tiles_m, int tiles) {
+    __shared__ __align__(16) int8_t xs[2][GB * kPitch];
+    __shared__ __align__(16) int8_t ws[2][GB * kPitch];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t M = a.M, N = a.N, K = a.K;
+
+    // consecutive workgroups go to consecutive XCDs: give XCD x the contiguous tile run
+    // [x*q + min(x, rem), ...) so that neighbouring tiles share an L2
+    const int b = blockIdx.x, q = tiles / 8, rem = tiles % 8, xcd = b % 8, slot = b / 8;
+    const int t = xcd * q + min(xcd, rem) + slot;
+    const int64_t m0 = (int64_t)(t % tiles_m) * GB, n0 = (int64_t)(t / tiles_m) * GB;
+
+    // staging: thread -> rows sr + 32 i, bytes [sc, sc + 16) of the stage.  Rows past M or N
+    // re-read the last valid row; they feed only outputs that are never stored.
+    const int sr = tid >> 3, sc = (tid & 7) * 16;
+    const int8_t *xrow[4], *wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int64_t mr = m0 + sr + 32 * i, nr = n0 + sr + 32 * i;
+        xrow[i] = a.x_q + (mr < M ? mr : M - 1) * K + sc;
+        wrow[i] = a.w_q + (nr < N ? nr : N - 1) * K + sc;
+    }
+    uint4 rx[4], rw[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        rx[i] = *reinterpret_cast<const uint4 *>(xrow[i]);
+        rw[i] = *reinterpret_cast<const uint4 *>(wrow[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        *reinterpret_cast<uint4 *>(&xs[0][(sr + 32 * i) * kPitch + sc]) = rx[i];
+        *reinterpret_cast<uint4 *>(&ws[0][(sr + 32 * i) * kPitch + sc]) = rw[i];
+    }
+    __syncthreads();
+
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hk = (lane >> 5) * 16;
+    int16v acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = int16v{};
+
+    const int nk = (int)(K / GK);
+    for (int kt = 0; kt < nk; kt++) {
+        const int buf = kt & 1;
+        // the next stage (the last stage again on the last step: loaded and stored into the
+        // idle buffer, never read), unconditional so the staging stays in registers
+        const int64_t k1 = (int64_t)(kt + 1 < nk ? kt + 1 : kt) * GK;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            rx[i] = *reinterpret_cast<const uint4 *>(xrow[i] + k1);
+            rw[i] = *reinterpret_cast<const uint4 *>(wrow[i] + k1);
+        }
+#pragma unroll
+        for (int s = 0; s < GK / 32; s++) {
+            int4v A[2], B[2];
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++)
+                A[ib] = *reinterpret_cast<const int4v *>(&xs[buf][(wm * 64 + ib * 32 + l32) * kPitch + s * 32 + hk]);
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++)
+                B[jb] = *reinterpret_cast<const int4v *>(&ws[buf][(wn * 64 + jb * 32 + l32) * kPitch + s * 32 + hk]);
+            // A and B lanes carry the same 16 k of the 32-wide step, so the product is the
+            // full sum over the step whatever order the unit takes them in
+#pragma unroll
+            for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+                for (int jb = 0; jb < 2; jb++)
+                    acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            *reinterpret_cast<uint4 *>(&xs[buf ^ 1][(sr + 32 * i) * kPitch + sc]) = rx[i];
+            *reinterpret_cast<uint4 *>(&ws[buf ^ 1][(sr + 32 * i) * kPitch + sc]) = rw[i];
+        }
+        __syncthreads();
+    }
+
+    // lane holds weight row j = l32 of each 32 x 32 block and tokens 8(v/4) + 4 half + v%4
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+        const int64_t r = n0 + wn * 64 + jb * 32 + l32;
+        if (r >= N) continue;
+        const float sw = a.s_w[r];
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t m = m0 + wm * 64 + ib * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M) {
+                    const float val = ((float)acc[ib][jb][v] * sw) * a.s_x[m];
+                    if (a.y_bf16)
+                        static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(val);
+                    else
+                        static_cast<float *>(a.y)[m * N + r] = val;
+                }
+            }
+    }
+}
+
+}  // namespace
+
+bool w8_gemv_supported(int64_t M, int64_t K) { return M >= 1 && M <= 4 && M * K <= kW8GemvMaxX; }
+
+hipError_t launch_w8_gemv(const W8Args &a, int num_cu, hipStream_t stream) {
+    int64_t grid = num_cu;
+    const int64_t need = (a.N + kGvMaxRows - 1) / kGvMaxRows;
+    if (grid < need) grid = need;
+    switch (a.M) {
+        case 1: hipLaunchKernelGGL(k_w8_gemv<1>, dim3((unsigned)grid), dim3(kGvThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(k_w8_gemv<2>, dim3((unsigned)grid), dim3(kGvThreads), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL(k_w8_gemv<3>, dim3((unsigned)grid), dim3(kGvThreads), 0, stream, a); break;
+        default: hipLaunchKernelGGL(k_w8_gemv<4>, dim3((unsigned)grid), dim3(kGvThreads), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_w8_gemm(const W8Args &a, hipStream_t stream) {
+    const int64_t tm = (a.M + GB - 1) / GB, tn = (a.N + GB - 1) / GB;
+    hipLaunchKernelGGL(k_w8_gemm, dim3((unsigned)(tm * tn)), dim3(kGmThreads), 0, stream, a, (int)tm,
+                       (int)(tm * tn));
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

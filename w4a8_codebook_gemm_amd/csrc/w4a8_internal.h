@@ -238,6 +238,22 @@ hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
 bool skinny_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream);
 
+// W8A8 comparator (per-row int8 weights of the rotated rows, no codebook)
+struct W8Args {
+    const int8_t *x_q;
+    const float *s_x;
+    int64_t M, K, N;
+    const int8_t *w_q;
+    const float *s_w;
+    void *y;
+    int y_bf16;
+};
+constexpr int64_t kW8GemvMaxX = 65536;   // M*K activation bytes the decode GEMV stages in LDS
+constexpr int64_t kW8MaxK = 131072;      // exact int32 sums: 127^2 * K < 2^31
+bool w8_gemv_supported(int64_t M, int64_t K);
+hipError_t launch_w8_gemv(const W8Args &a, int num_cu, hipStream_t stream);
+hipError_t launch_w8_gemm(const W8Args &a, hipStream_t stream);
+
 size_t quantize_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint64_t seed,
                            int8_t *packed, uint8_t *s_rel, float *s_ch, float *cb,
