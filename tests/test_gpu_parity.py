@@ -243,8 +243,10 @@ def test_mfma_i8_full_size_sampled(w, N, K):
     i8_tight(y, q, xq, sx, rows, toks)
 
 
+# 256-token x 192-row tiles: ragged in both directions, several tiles each way, K = 256 (one
+# turn of the four-stage ring)
 @pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (512, 256, 257),
-                                   (17, 5120, 3)])
+                                   (17, 5120, 3), (385, 1280, 600), (193, 256, 65), (1000, 2048, 513)])
 def test_mfma_f16_parity(w, N, K, M):
     say(f"mfma_f16 N={N} K={K} M={M}")
     y, yr, A, _ = run_linear(w, w.ALGO_MFMA_F16, N, K, M, n_out=2)

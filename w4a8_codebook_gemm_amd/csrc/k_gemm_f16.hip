@@ -7,23 +7,30 @@
 //
 // Each weight is decoded once per tile to fp16 w16 = fp16(s16 * cb16[idx]) with
 // cb16 = fp16(cb / 2^ex) (max |cb| = f 2^ex, f in [0.5, 1)) and s16 = s_rel * 2^8 (exact:
-// an e4m3 value times a power of two).  Two fp16 roundings give at most ~2^-10 relative
-// error per weight, inside the layer's 4e-3 * sum |x w| bound by construction; the 2^8
-// keeps products of small scales and levels out of the fp16 subnormal range.  x_q is exact
-// in fp16.  With the group scale inside the weight, every group accumulates into the same
-// fp32 MFMA accumulator: no per-group fold on the vector ALU.
+// an e4m3 value times a power of two; s_rel <= 1 in this format, so s16 <= 256).  Two fp16
+// roundings give at most ~2^-10 relative error per weight, inside the layer's
+// 4e-3 * sum |x w| bound by construction; the 2^8 keeps products of small scales and
+// levels out of the fp16 subnormal range.  x_q is exact in fp16.  With the group scale
+// inside the weight, every group accumulates into the same fp32 MFMA accumulator: no
+// per-group fold on the vector ALU.
 //   y[m, r] = acc * 2^(ex - 8) * s_channel[r] * s_x[m].
 //
-// Tile: 128 tokens x 256 rows per 256-thread workgroup; waves 2 (tokens) x 2 (rows), each
-// 64 x 128 = 2 x 4 fragments of v_mfma_f32_32x32x16_f16 (one 16-k group per MFMA).  K
-// steps of 64 are staged through double-buffered LDS:
-//  * activations as fp16, [token][64 + 8 pad] (16-B fragment reads spread over the banks);
-//  * the fp16 codebook-pair table (256 packed-byte values x 32 columns, 256-B rows) as in
-//    the decode GEMV: one v_perm address + one ds_read_b32 per packed byte;
-//  * the packed indices and the fp16x2 group scales in the unused second half of every
-//    table row, stored [k-slot][row] so that a fragment's 32 lanes read 32 consecutive
-//    dwords.
-#include <algorithm>
+// Tile: 256 tokens x 192 weight rows per 512-thread workgroup, one workgroup per CU (the
+// 192-row tile divides both MLP shapes into nearly whole rounds of 256 tiles).  Waves
+// 4 (tokens) x 2 (rows), each 64 x 96 = 2 x 3 fragments of v_mfma_f32_32x32x16_f16.  K
+// advances in stages of 64, double-buffered through LDS; the global loads run four stages
+// ahead in a ring of register stages, so a stage is decoded three steps after its loads
+// were issued:
+//  * activations: int8 -> fp16 once per stage (exact, v_perm onto 0x6400 then one packed
+//    subtract) into [token][64 + 8 pad] rows;
+//  * weights: decoded once per stage by the whole workgroup -- a packed byte indexes a
+//    256-entry LDS table of fp16 pairs (cb16[low nibble], cb16[high nibble]), one packed
+//    multiply applies the group scale -- into [row][64 + 8 pad] rows, so the MFMA loop
+//    reads plain fp16 fragments for both operands.
+// The 144-byte LDS rows put the 16 rows one 16-lane phase of a 16-byte fragment read
+// touches on 16 distinct 16-byte bank quads of the 64 banks.  Tiles are numbered so that
+// each XCD works through a contiguous run, token tiles fastest: the workgroups resident on
+// one XCD share weight and activation stages through its L2.
 #include <type_traits>
 
 #include "w4a8_internal.h"
@@ -34,164 +41,175 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int kThreads = 256;
-constexpr int kXRow = BK + 8;                      // fp16 per staged activation row (padded)
-constexpr int kXTile = BM * kXRow;                 // fp16 per activation stage
-constexpr int kTabBytes = 256 * 256;               // pair table rows of 256 B
-// hole space (second 128 B of each table row): per stage 8 KiB packed + 4 KiB scales
-constexpr int kPkBytes = BN * BK / 2;              // [8 k-slots][BN rows] dwords
-constexpr int kSsBytes = BN * (BK / kGroup) * 4;   // [4 groups][BN rows] fp16x2
-constexpr int kStageHole = kPkBytes + kSsBytes;
+constexpr int BM = 256, BN = 192, BK = 64;
+constexpr int kThreads = 512;
+constexpr int JB = BN / 64;                    // 32-row weight fragments per wave
+constexpr int kPitch = BK + 8;                 // fp16 per LDS row (144 B)
+constexpr int kXStage = BM * kPitch, kBStage = BN * kPitch;
 
-__device__ __forceinline__ uint32_t lds_u32(const char *base, uint32_t byte_addr) {
-    return *reinterpret_cast<const uint32_t *>(base + byte_addr);
+// four int8 -> four fp16 (exact): bytes b ^ 0x80 under the fp16 exponent of 1024 give
+// 1024 + b + 128; subtracting 1152 leaves b
+__device__ __forceinline__ uint2 i8x4_to_f16x4(uint32_t v) {
+    const uint32_t t = v ^ 0x80808080u;
+    const half2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const half2_t lo = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u)) - off;
+    const half2_t hi = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u)) - off;
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-__global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a) {
-    __shared__ __align__(16) char tab[kTabBytes];                 // table + holes
-    __shared__ __align__(16) _Float16 xs[2][kXTile];
+struct Stage {
+    uint4 x0, x1;   // 32 activation bytes of token xr
+    uint4 p;        // 32 packed indices of weight row pr (two groups)
+    uint32_t s;     // the row's four e4m3 group scales of the stage
+};
+
+template <int J>
+using IC = std::integral_constant<int, J>;
+
+__global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m, int tiles) {
+    __shared__ __align__(16) _Float16 xs[2][kXStage];
+    __shared__ __align__(16) _Float16 bs[2][kBStage];
+    __shared__ uint32_t tab[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
 
-    // ---- staging assignment (rows past M or N read as zero via buffer bounds)
-    const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
-    const int64_t nvalid = std::min<int64_t>(BN, N - n0), mvalid = std::min<int64_t>(BM, M - m0);
-    const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.x_q + m0 * K), (short)0, (int)(mvalid * K), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.packed + n0 * rowbytes), (short)0, (int)(nvalid * rowbytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.s_rel + n0 * grpbytes), (short)0, (int)(nvalid * grpbytes), 0x00020000);
-    const int xr = tid >> 1, xh = tid & 1;     // activations: token xr, 32 values at 32 xh
-    const int pr = tid;                        // packed + scales: row pr (32 B + 4 codes)
+    // consecutive workgroups go to consecutive XCDs: XCD x takes the contiguous tile run
+    // starting at x*q + min(x, rem)
+    const int b = blockIdx.x, q = tiles / 8, rem = tiles % 8, xcd = b % 8, slot = b / 8;
+    const int t = xcd * q + min(xcd, rem) + slot;
+    const int64_t m0 = (int64_t)(t % tiles_m) * BM, n0 = (int64_t)(t / tiles_m) * BN;
 
-    // ---- codebook pair table: cb16 = fp16(cb / 2^ex); entry e at e*256 + 4*column
+    // ---- codebook pair table: cb16 = fp16(cb / 2^ex); entry e = (cb16[e & 15], cb16[e >> 4])
     float cmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < kLevels; j++) cmax = fmaxf(cmax, fabsf(a.cb[j]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
-    const float inv = ldexpf(1.0f, -ex);
-    {
-        const int e0 = tid;  // 256 threads: one entry each, 32 columns
-        const uint32_t v = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e0 & 15] * inv)) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e0 >> 4] * inv)) << 16);
-        uint4 *row = reinterpret_cast<uint4 *>(tab + e0 * 256);
-#pragma unroll
-        for (int c = 0; c < 8; c++) row[c] = make_uint4(v, v, v, v);
+    if (tid < 256) {
+        const float inv = ldexpf(1.0f, -ex);
+        tab[tid] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[tid & 15] * inv)) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[tid >> 4] * inv)) << 16);
     }
 
-    // Global loads run two K steps ahead of their use, in two register sets: the loads for
-    // step s are issued at the start of step s-2 and written to LDS at the end of step s-1.
-    struct Stage {
-        u32x4_t x0, x1, p0, p1;
-        uint32_t s;
+    // ---- staging roles: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight row pr,
+    // weights [32 ph, 32 ph + 32) (two groups).  Rows past M or N re-read the last valid row:
+    // they feed only outputs that are never stored.  Threads past 2 BN load like the last
+    // row's but decode nothing.
+    const int xr = tid >> 1, xh = tid & 1;
+    const int pr0 = tid >> 1, ph = tid & 1;
+    const bool pdec = pr0 < BN;                    // wave-uniform: 2 BN is a multiple of 64
+    const int pr = pdec ? pr0 : BN - 1;
+    const int8_t *xp = a.x_q + min<int64_t>(m0 + xr, M - 1) * K + 32 * xh;
+    const int64_t wrow = min<int64_t>(n0 + pr, N - 1);
+    const int8_t *pp = a.packed + wrow * (K / 2) + 16 * ph;
+    // a row's group scales start 16-byte aligned (K / 16 is a multiple of 16); one dword
+    // holds the stage's four
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(a.s_rel + wrow * (K / kGroup));
+    const int sshift = 16 * ph;
+    const int nk = (int)(K / BK);
+
+    // every stage's loads are issued unconditionally (stages past the end re-read the last
+    // one) so that the in-order load counter lets a decode wait for its own stage only
+    auto gload = [&](int kt, Stage &st) {
+        const int k = kt < nk ? kt : nk - 1;
+        st.x0 = *reinterpret_cast<const uint4 *>(xp + (int64_t)k * BK);
+        st.x1 = *reinterpret_cast<const uint4 *>(xp + (int64_t)k * BK + 16);
+        st.p = *reinterpret_cast<const uint4 *>(pp + (int64_t)k * (BK / 2));
+        st.s = sp[k];
     };
-    auto gload = [&](int64_t k0, Stage &st) {
-        const uint32_t xo = (uint32_t)(xr * K + k0 + 32 * xh);
-        st.x0 = __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo, 0, 0);
-        st.x1 = __builtin_amdgcn_raw_buffer_load_b128(rs_x, xo + 16, 0, 0);
-        const uint32_t po = (uint32_t)(pr * rowbytes + k0 / 2);
-        st.p0 = __builtin_amdgcn_raw_buffer_load_b128(rs_p, po, 0, 0);
-        st.p1 = __builtin_amdgcn_raw_buffer_load_b128(rs_p, po + 16, 0, 0);
-        st.s = __builtin_amdgcn_raw_buffer_load_b32(rs_s, (uint32_t)(pr * grpbytes + k0 / kGroup), 0, 0);
-    };
-    auto cvt2 = [](uint32_t v, int sh) {  // two int8 -> fp16x2 (exact)
-        return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> sh) & 0xFF)) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(int8_t)((v >> (sh + 8)) & 0xFF)) << 16);
-    };
-    // Hole space of stage b: k-slot s (= 2 g + h) of row r at dword (s * BN + r), then the
-    // scales of group g of row r at dword (kPkBytes / 4 + g * BN + r).  A dword index d maps
-    // to LDS byte (d / 32) * 256 + 128 + (d % 32) * 4.  Writer: row pr; readers: row
-    // wn*128 + jb*32 + l32.  Both reduce to a per-lane base plus compile-time offsets.
-    char *const st_base = tab + ((pr >> 5) << 8) + 128 + ((pr & 31) << 2);
-    auto lstore = [&](int buf, const Stage &st) {
-        uint4 *dx = reinterpret_cast<uint4 *>(&xs[buf][xr * kXRow + 32 * xh]);
-        const uint32_t w[8] = {st.x0.x, st.x0.y, st.x0.z, st.x0.w, st.x1.x, st.x1.y, st.x1.z, st.x1.w};
+    _Float16 *const xdst = &xs[0][xr * kPitch + 32 * xh];
+    _Float16 *const bdst = &bs[0][pr * kPitch + 32 * ph];
+    auto lstore = [&](auto bufc, const Stage &st) {
+        constexpr int buf = decltype(bufc)::value;
+        const uint32_t xw[8] = {st.x0.x, st.x0.y, st.x0.z, st.x0.w, st.x1.x, st.x1.y, st.x1.z, st.x1.w};
+        uint4 *dx = reinterpret_cast<uint4 *>(xdst + buf * kXStage);
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            dx[q] = make_uint4(cvt2(w[2 * q], 0), cvt2(w[2 * q], 16), cvt2(w[2 * q + 1], 0), cvt2(w[2 * q + 1], 16));
-        char *sb = st_base + buf * (2 * kStageHole);  // hole bytes map 128 -> 256
-        const uint32_t p[8] = {st.p0.x, st.p0.y, st.p0.z, st.p0.w, st.p1.x, st.p1.y, st.p1.z, st.p1.w};
+        for (int i = 0; i < 4; i++) {
+            const uint2 c0 = i8x4_to_f16x4(xw[2 * i]), c1 = i8x4_to_f16x4(xw[2 * i + 1]);
+            dx[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        }
+        if (pdec) {
+            const uint32_t sv = st.s >> sshift;
+            const _Float16 s0 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 0) * 256.0f);
+            const _Float16 s1 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 1) * 256.0f);
+            const half2_t g0 = {s0, s0}, g1 = {s1, s1};
+            const uint32_t pw[4] = {st.p.x, st.p.y, st.p.z, st.p.w};
+            uint32_t o[16];
 #pragma unroll
-        for (int k = 0; k < 8; k++) *reinterpret_cast<uint32_t *>(sb + k * (BN / 32) * 256) = p[k];
-        const float sv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)st.s, 0), __builtin_amdgcn_cvt_f32_fp8((int)st.s, 1),
-                             __builtin_amdgcn_cvt_f32_fp8((int)st.s, 2), __builtin_amdgcn_cvt_f32_fp8((int)st.s, 3)};
+            for (int i = 0; i < 16; i++) {
+                const half2_t pair = __builtin_bit_cast(half2_t, tab[(pw[i >> 2] >> (8 * (i & 3))) & 0xFFu]);
+                o[i] = __builtin_bit_cast(uint32_t, pair * (i < 8 ? g0 : g1));
+            }
+            uint4 *db = reinterpret_cast<uint4 *>(bdst + buf * kBStage);
 #pragma unroll
-        for (int g = 0; g < 4; g++) {  // group scale as fp16x2, times 2^8
-            const uint32_t h16 = __builtin_bit_cast(uint16_t, (_Float16)(sv[g] * 256.0f));
-            *reinterpret_cast<uint32_t *>(sb + (kPkBytes / 128) * 256 + g * (BN / 32) * 256) = h16 | (h16 << 16);
+            for (int i = 0; i < 4; i++) db[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
         }
     };
 
-    float16_t acc[2][4];
+    float16_t acc[2][JB];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < JB; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-    const int nk = (int)(K / BK);
-    Stage R0, R1;  // register stages for even / odd K steps (compile-time selected)
+    Stage R0, R1, R2, R3;
     gload(0, R0);
-    if (nk > 1) gload(BK, R1);
-    lstore(0, R0);
+    gload(1, R1);
+    gload(2, R2);
+    gload(3, R3);
     __syncthreads();
-    const int half = lane >> 5, l32 = lane & 31;
-    const uint32_t lanebase = (uint32_t)l32 * 4u;
-    const char *rd_base = tab + ((wn * 128) >> 5) * 256 + 128 + l32 * 4 + half * (BN / 32) * 256;
+    lstore(IC<0>{}, R0);
+    __syncthreads();
 
-    // one K step on LDS stage BUF, with R the register stage of this step's parity
-    auto kstep = [&](int kt, auto bufc, Stage &Rcur, Stage &Rnext) {
+    const int half = lane >> 5, l32 = lane & 31;
+    const _Float16 *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 8 * half];
+    const _Float16 *const brd = &bs[0][(wn * (BN / 2) + l32) * kPitch + 8 * half];
+
+    auto mfmas = [&](auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        if (kt + 2 < nk) gload((int64_t)(kt + 2) * BK, Rcur);
-        const char *rb = rd_base + buf * (2 * kStageHole);
 #pragma unroll
-        for (int g = 0; g < BK / kGroup; g++) {
-            half8_t A[2];
+        for (int g = 0; g < BK / 16; g++) {
+            half8_t A[2], B[JB];
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++) {
-                const int row = wm * 64 + ib * 32 + l32;
-                A[ib] = *reinterpret_cast<const half8_t *>(&xs[buf][row * kXRow + g * kGroup + 8 * half]);
-            }
+            for (int ib = 0; ib < 2; ib++)
+                A[ib] = *reinterpret_cast<const half8_t *>(xrd + buf * kXStage + ib * 32 * kPitch + g * 16);
 #pragma unroll
-            for (int jb = 0; jb < 4; jb++) {
-                const uint32_t pk = *reinterpret_cast<const uint32_t *>(rb + (2 * g) * (BN / 32) * 256 + jb * 256);
-                const uint32_t s2 = *reinterpret_cast<const uint32_t *>(
-                    rb - half * (BN / 32) * 256 + (kPkBytes / 128) * 256 + g * (BN / 32) * 256 + jb * 256);
-                uint32_t bw[4];
+            for (int jb = 0; jb < JB; jb++)
+                B[jb] = *reinterpret_cast<const half8_t *>(brd + buf * kBStage + jb * 32 * kPitch + g * 16);
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const uint32_t pair = lds_u32(tab, __builtin_amdgcn_perm(lanebase, pk, 0x0C0C0004u | (i << 8)));
-                    bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair) * __builtin_bit_cast(half2_t, s2));
-                }
-                const half8_t B = __builtin_bit_cast(half8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+            for (int ib = 0; ib < 2; ib++)
 #pragma unroll
-                for (int ib = 0; ib < 2; ib++)
-                    acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[ib], B, acc[ib][jb], 0, 0, 0);
-            }
+                for (int jb = 0; jb < JB; jb++)
+                    acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
         }
-        // the other stage's readers finished before the previous step's barrier
-        if (kt + 1 < nk) lstore(buf ^ 1, Rnext);
+    };
+    // step s (ring slot J = s % 4): its stage is in LDS buffer J % 2; the slot reloads stage
+    // s + 4; stage s + 1 (loaded three steps ago) is decoded into the other buffer
+    auto step = [&](int s, auto jc, Stage &Rcur, Stage &Rnext) {
+        constexpr int J = decltype(jc)::value;
+        gload(s + 4, Rcur);
+        lstore(IC<(J + 1) % 2>{}, Rnext);
+        mfmas(IC<J % 2>{});
         __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-        kstep(kt, std::integral_constant<int, 0>{}, R0, R1);
-        if (kt + 1 < nk) kstep(kt + 1, std::integral_constant<int, 1>{}, R1, R0);
+    // nk = K / 64 is a multiple of 4 (K is a multiple of 256): whole ring turns only
+    for (int s = 0; s < nk; s += 4) {
+        step(s, IC<0>{}, R0, R1);
+        step(s + 1, IC<1>{}, R1, R2);
+        step(s + 2, IC<2>{}, R2, R3);
+        step(s + 3, IC<3>{}, R3, R0);
     }
 
     // ---- epilogue: lane holds column j = l32 (weight row), tokens 8(v/4) + 4 half + v%4
     const float scale = ldexpf(1.0f, ex - 8);
 #pragma unroll
-    for (int jb = 0; jb < 4; jb++) {
-        const int64_t r = n0 + wn * 128 + jb * 32 + l32;
+    for (int jb = 0; jb < JB; jb++) {
+        const int64_t r = n0 + wn * (BN / 2) + jb * 32 + l32;
         if (r >= N) continue;
         const float rsc = a.s_ch[r] * scale;
 #pragma unroll
@@ -213,8 +231,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a) {
 }  // namespace
 
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream) {
-    dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-    hipLaunchKernelGGL(k_gemm_f16, grid, dim3(kThreads), 0, stream, a);
+    const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    hipLaunchKernelGGL(k_gemm_f16, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, a, (int)tm,
+                       (int)(tm * tn));
     return hipGetLastError();
 }
 
