@@ -20,7 +20,8 @@ matrices) / measured time per step.  The same line carries:
   sweep         batched decode: M in {1,2,4,8,16,32,64} x four projection shapes, every
                 kernel that supports the point, plus the automatic choice (prepare included);
   model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
-                token = 248 fused forwards + 248 prepared-input linears from one HIP graph;
+                token = one fused multi-layer call per input (248 launches) from one HIP graph,
+                and the same token with one launch per projection (496);
   prefill       M=2048 GEMMs on both MLP shapes: int8-MFMA (per-16 fold) and f16-MFMA;
   w8a8          the INT8 ConvRot comparator (same rotation and int8 activations, per-row
                 int8 weights): decode GEMV on both MLP shapes (prepared x_q), a decode step
@@ -295,8 +296,9 @@ def model(w, torch, S, tokens=20):
     """62 layers x (gate, up 17408x5120; down 5120x17408; five 5120x5120): one token reads every
     weight once.  Inputs per layer: the attention input feeds four square projections, the
     attention output the fifth; the MLP input feeds gate and up; the MLP hidden feeds down.
-    The first projection of each input runs the fused forward (it writes x_q, s_x), the others
-    reuse x_q through w4a8_linear."""
+    Each input is one fused call: w4a8_forward_multi over the layers that read it (4 launches
+    per layer).  For comparison, the same token with one launch per projection: the fused
+    forward for the first projection of each input, w4a8_linear on its x_q for the others."""
     base = {}
     for sh in (S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE):
         W = torch.from_numpy(S.weights(*sh, seed=0)).cuda()
@@ -317,7 +319,18 @@ def model(w, torch, S, tokens=20):
                 torch.empty((1,), dtype=torch.float32, device="cuda")) for key, v in xs.items()}
     y5, y17 = (torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (d, S.MLP_GATE_UP[0]))
 
+    y5s = [torch.empty((1, d), dtype=torch.float32, device="cuda") for _ in range(4)]
+    y17s = [torch.empty((1, S.MLP_GATE_UP[0]), dtype=torch.float32, device="cuda") for _ in range(2)]
+
     def token():
+        for L in layers:
+            w.forward_multi(xs["attn_in"], L["attn"][:4], outs=y5s, x_q=xq["attn_in"][0], s_x=xq["attn_in"][1])
+            w.forward(xs["attn_out"], L["attn"][4], out=y5, x_q=xq["attn_out"][0], s_x=xq["attn_out"][1])
+            w.forward_multi(xs["mlp_in"], [L["gate"], L["up"]], outs=y17s, x_q=xq["mlp_in"][0],
+                            s_x=xq["mlp_in"][1])
+            w.forward(xs["mlp_hid"], L["down"], out=y5, x_q=xq["mlp_hid"][0], s_x=xq["mlp_hid"][1])
+
+    def token_separate():
         for L in layers:
             w.forward(xs["attn_in"], L["attn"][0], out=y5, x_q=xq["attn_in"][0], s_x=xq["attn_in"][1])
             for j in (1, 2, 3):
@@ -327,16 +340,23 @@ def model(w, torch, S, tokens=20):
             w.linear(*xq["mlp_in"], L["up"], out=y17)
             w.forward(xs["mlp_hid"], L["down"], out=y5, x_q=xq["mlp_hid"][0], s_x=xq["mlp_hid"][1])
 
-    g = make_graph(torch, token)
-    g.replay()
-    torch.cuda.synchronize()
-    t = time_graph(torch, g, tokens)
+    res = {}
+    for name, fn in (("multi", token), ("separate", token_separate)):
+        g = make_graph(torch, fn)
+        g.replay()
+        torch.cuda.synchronize()
+        res[name] = time_graph(torch, g, tokens)
+        del g
+    t, t_sep = res["multi"], res["separate"]
     log(f"model: {MODEL_LAYERS} layers, {total / 1e9:.2f} GB, {t * 1e3:.3f} ms/token, "
-        f"{1 / t:.1f} tokens/s, {total / t / 1e9:.1f} GB/s")
-    out = dict(layers=MODEL_LAYERS, projections_per_layer=8, launches_per_token=8 * MODEL_LAYERS,
+        f"{1 / t:.1f} tokens/s, {total / t / 1e9:.1f} GB/s (one launch per projection: "
+        f"{t_sep * 1e3:.3f} ms/token, {1 / t_sep:.1f} tokens/s)")
+    out = dict(layers=MODEL_LAYERS, projections_per_layer=8, launches_per_token=4 * MODEL_LAYERS,
                weight_bytes=total, ms_per_token=round(t * 1e3, 4), tokens_per_s=round(1 / t, 1),
-               weight_gbs=round(total / t / 1e9, 1), hbm_bound_tokens_per_s=round(HBM_PEAK_GBS * 1e9 / total, 1))
-    del layers, base, g
+               weight_gbs=round(total / t / 1e9, 1), hbm_bound_tokens_per_s=round(HBM_PEAK_GBS * 1e9 / total, 1),
+               one_launch_per_projection=dict(launches_per_token=8 * MODEL_LAYERS, ms_per_token=round(t_sep * 1e3, 4),
+                                              tokens_per_s=round(1 / t_sep, 1)))
+    del layers, base
     return out
 
 

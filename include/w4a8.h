@@ -173,6 +173,43 @@ W4A8_API int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, cons
 W4A8_API int w4a8_linear_pick(int64_t M, int64_t N, int64_t K);
 
 /*
+ * One quantised layer for the multi-layer calls below: its four tensors, its row count and
+ * its output [M][N].  Device pointers, as everywhere.
+ */
+typedef struct {
+    const int8_t *packed;       /* [N][K/2] */
+    const uint8_t *s_rel;       /* [N][K/16] */
+    const float *s_channel;     /* [N] */
+    const float *codebook;      /* [16] */
+    int64_t N;                  /* rows, >= 1 */
+    void *y;                    /* [M][N] output, element type y_dtype */
+} w4a8_layer;
+
+/*
+ * Several layers that read the same activations (the query/key/value projections of one
+ * input, or gate and up) in one call [card "...w4a8-convrot-ComfyUI", section "Why this
+ * exists": decode re-reads every weight for every token, so each launch's fixed cost is paid
+ * once per layer per token].  For GEMV sizes (M <= 4 and M*K <= 40960) all layers run in ONE
+ * launch, its workgroups split between the layers in proportion to their rows; otherwise
+ * each layer runs as w4a8_linear would.  Every y is bit-identical to what w4a8_linear gives
+ * for that layer alone.
+ *
+ *  layers   HOST array of G descriptors, 1 <= G <= 8; read during the call only
+ *  others   as for w4a8_linear; each layer is validated like a w4a8_linear call
+ */
+W4A8_API int w4a8_linear_multi(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, int G,
+                               const w4a8_layer *layers, int y_dtype, void *stream);
+
+/*
+ * Activation preparation and several layers in one call: the results of
+ * w4a8_prepare_activation followed by w4a8_linear_multi, bit for bit.  For the fused decode
+ * sizes of w4a8_forward everything runs in ONE launch.  x_q [M][K] and s_x [M] are outputs.
+ */
+W4A8_API int w4a8_forward_multi(const void *x, int x_dtype, int64_t M, int64_t K, int G,
+                                const w4a8_layer *layers, int y_dtype, int8_t *x_q, float *s_x,
+                                void *stream);
+
+/*
  * W8A8 comparator: the "INT8 ConvRot" build the W4A8 format is weighed against [card
  * "...w4a8-convrot-ComfyUI", section "Why this exists": an INT8 ConvRot build of the model
  * takes about twice the weight bytes, and W4A8 runs on the same int8 GEMM path plus a

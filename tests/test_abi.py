@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 11 and set(names) == set(w.EXPORTS)
+    assert len(names) == 13 and set(names) == set(w.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 
@@ -152,3 +152,32 @@ def test_w8a8_validation(L):
     assert lin8(algo=w.ALGO_MFMA_SKINNY) == 3
     assert lin8(M=5, algo=w.ALGO_GEMV) == 2              # GEMV: M <= 4
     assert lin8(M=4, K=16640, algo=w.ALGO_GEMV) == 2     # GEMV: M*K <= 65536
+
+
+def test_multi_validation(L):
+    def table(G, **bad):
+        t = (w.Layer * max(G, 1))()
+        for g in range(max(G, 1)):
+            t[g] = w.Layer(FAKE, FAKE, FAKE, FAKE, 256, FAKE)
+        for k, v in bad.items():
+            setattr(t[0], k, v)
+        return t
+
+    def lin(G=2, t=None, M=1, K=512, ydt=0, xq=FAKE):
+        t = table(G) if t is None else t
+        return L.w4a8_linear_multi(xq, FAKE, M, K, G, C.addressof(t), ydt, None)
+
+    assert L.w4a8_linear_multi(FAKE, FAKE, 1, 512, 2, None, 0, None) == 1
+    assert lin(G=0) == 2 and lin(G=9) == 2
+    assert lin(t=table(2, packed=0)) == 1
+    assert lin(t=table(2, y=MIS)) == 4
+    assert lin(t=table(2, N=0)) == 2
+    assert lin(K=300) == 2
+    assert lin(ydt=5) == 3
+    assert lin(xq=0) == 1
+    f = L.w4a8_forward_multi
+    t = table(2)
+    assert f(0, 0, 1, 512, 2, C.addressof(t), 0, FAKE, FAKE, None) == 1
+    assert f(FAKE, 4, 1, 512, 2, C.addressof(t), 0, FAKE, FAKE, None) == 3
+    assert f(MIS, 0, 1, 512, 2, C.addressof(t), 0, FAKE, FAKE, None) == 4
+    assert f(FAKE, 0, 1, 512, 2, C.addressof(t), 0, 0, FAKE, None) == 1

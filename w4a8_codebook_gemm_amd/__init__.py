@@ -28,8 +28,15 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN"
           5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
            "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
-           "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward", "w4a8_w8a8_quantize_weight",
-           "w4a8_w8a8_linear")
+           "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward", "w4a8_linear_multi",
+           "w4a8_forward_multi", "w4a8_w8a8_quantize_weight", "w4a8_w8a8_linear")
+MAX_GROUP = 8
+
+
+class Layer(C.Structure):
+    """w4a8_layer: one layer's device pointers, rows and output pointer."""
+    _fields_ = [("packed", C.c_void_p), ("s_rel", C.c_void_p), ("s_channel", C.c_void_p),
+                ("codebook", C.c_void_p), ("N", C.c_int64), ("y", C.c_void_p)]
 
 
 class W4A8Error(RuntimeError):
@@ -67,6 +74,10 @@ def lib():
         L.w4a8_linear_pick.restype = i32
         L.w4a8_forward.argtypes = [P, i32, i64, i64, P, P, P, P, i64, P, i32, P, P, P]
         L.w4a8_forward.restype = i32
+        L.w4a8_linear_multi.argtypes = [P, P, i64, i64, i32, P, i32, P]
+        L.w4a8_linear_multi.restype = i32
+        L.w4a8_forward_multi.argtypes = [P, i32, i64, i64, i32, P, i32, P, P, P]
+        L.w4a8_forward_multi.restype = i32
         L.w4a8_w8a8_quantize_weight.argtypes = [P, i32, i64, i64, P, P, P]
         L.w4a8_w8a8_quantize_weight.restype = i32
         L.w4a8_w8a8_linear.argtypes = [P, P, i64, i64, P, P, i64, P, i32, i32, P]
@@ -216,6 +227,59 @@ def forward(x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32, ou
                               _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)),
                               _stream()), "w4a8_forward")
     return out
+
+
+def _layer_table(layers, m, k, out_dtype, outs):
+    if not 1 <= len(layers) <= MAX_GROUP:
+        raise ValueError(f"1 to {MAX_GROUP} layers per call, got {len(layers)}")
+    if outs is None:
+        outs = [None] * len(layers)
+    table = (Layer * len(layers))()
+    ys = []
+    for g, (L, y) in enumerate(zip(layers, outs)):
+        n = L.packed.shape[0]
+        if (tuple(L.packed.shape) != (n, k // 2) or tuple(L.s_rel.shape) != (n, k // 16)
+                or tuple(L.s_channel.shape) != (n,) or tuple(L.codebook.shape) != (16,)):
+            raise ValueError(f"layer {g}: tensors do not match in_features {k}")
+        if y is None:
+            y = torch.empty((m, n), dtype=out_dtype, device=L.packed.device)
+        table[g] = Layer(_dev(L.packed, "packed", (torch.int8,)), _dev(L.s_rel, "s_rel", (torch.uint8,)),
+                         _dev(L.s_channel, "s_channel", (torch.float32,)),
+                         _dev(L.codebook, "codebook", (torch.float32,)), n,
+                         _dev(y, "y", (torch.float32, torch.bfloat16)))
+        ys.append(y)
+    dt = {_fdtype(y) for y in ys}
+    if len(dt) != 1:
+        raise ValueError("all outputs of one call must have the same dtype")
+    return table, ys, dt.pop()
+
+
+def linear_multi(x_q: torch.Tensor, s_x: torch.Tensor, layers, out_dtype=torch.float32, outs=None):
+    """The product of prepared activations with several layers (one launch at GEMV sizes)."""
+    m, k = x_q.shape
+    if tuple(s_x.shape) != (m,):
+        raise ValueError("s_x must be [M]")
+    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs)
+    _check(lib().w4a8_linear_multi(_dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
+                                   len(ys), C.addressof(table), ydt, _stream()), "w4a8_linear_multi")
+    return ys
+
+
+def forward_multi(x: torch.Tensor, layers, out_dtype=torch.float32, outs=None, x_q=None, s_x=None):
+    """prepare_activation + linear_multi (one launch for the fused decode sizes)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    xp = _dev(x, "x", (torch.float32, torch.bfloat16))
+    if x_q is None:
+        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
+    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs)
+    _check(lib().w4a8_forward_multi(xp, _fdtype(x), m, k, len(ys), C.addressof(table), ydt,
+                                    _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)),
+                                    _stream()), "w4a8_forward_multi")
+    return ys
 
 
 def linear_pick(m: int, n: int, k: int) -> int:

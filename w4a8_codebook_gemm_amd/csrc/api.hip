@@ -166,6 +166,64 @@ int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, const int8_t 
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 
+// Validates G and every layer; fills the internal descriptors.
+static int check_multi(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, int G,
+                       const w4a8_layer *layers, int y_dtype, w4a8::LayerDesc *out) {
+    if (!layers) return W4A8_ERR_NULL;
+    if (G < 1 || G > w4a8::kMaxGroup) return W4A8_ERR_SHAPE;
+    for (int g = 0; g < G; g++) {
+        const w4a8_layer &l = layers[g];
+        int st = check_linear(x_q, s_x, M, K, l.packed, l.s_rel, l.s_channel, l.codebook, l.N, l.y, y_dtype);
+        if (st != W4A8_OK) return st;
+        out[g] = w4a8::LayerDesc{l.packed, l.s_rel, l.s_channel, l.codebook, l.N, l.y};
+    }
+    return W4A8_OK;
+}
+
+int w4a8_linear_multi(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, int G,
+                      const w4a8_layer *layers, int y_dtype, void *stream) {
+    w4a8::LayerDesc d[w4a8::kMaxGroup];
+    int st = check_multi(x_q, s_x, M, K, G, layers, y_dtype, d);
+    if (st != W4A8_OK) return st;
+    if (!w4a8::gemv_supported(M, K)) {
+        for (int g = 0; g < G; g++) {
+            st = w4a8_linear(x_q, s_x, M, K, d[g].packed, d[g].s_rel, d[g].s_ch, d[g].cb, d[g].N, d[g].y,
+                             y_dtype, stream);
+            if (st != W4A8_OK) return st;
+        }
+        return W4A8_OK;
+    }
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    w4a8::LinearArgs a{x_q, s_x, M, K, 0, nullptr, nullptr, nullptr, nullptr, nullptr, y_dtype == W4A8_BF16,
+                       nullptr, 0, nullptr, nullptr};
+    hipError_t e = w4a8::launch_gemv_multi(a, d, G, num_cu, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+int w4a8_forward_multi(const void *x, int x_dtype, int64_t M, int64_t K, int G, const w4a8_layer *layers,
+                       int y_dtype, int8_t *x_q, float *s_x, void *stream) {
+    if (!x) return W4A8_ERR_NULL;
+    w4a8::LayerDesc d[w4a8::kMaxGroup];
+    int st = check_multi(x_q, s_x, M, K, G, layers, y_dtype, d);
+    if (st != W4A8_OK) return st;
+    if (!valid_dtype(x_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(x)) return W4A8_ERR_ALIGN;
+    if (!w4a8::gemv_fused_supported(M, K)) {
+        st = w4a8_prepare_activation(x, x_dtype, M, K, x_q, s_x, stream);
+        if (st != W4A8_OK) return st;
+        return w4a8_linear_multi(x_q, s_x, M, K, G, layers, y_dtype, stream);
+    }
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    w4a8::LinearArgs a{x_q, s_x, M, K, 0, nullptr, nullptr, nullptr, nullptr, nullptr, y_dtype == W4A8_BF16,
+                       x, x_dtype == W4A8_BF16, x_q, s_x};
+    hipError_t e = w4a8::launch_gemv_fused_multi(a, d, G, num_cu, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
 int w4a8_w8a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, int8_t *w_q,
                               float *s_w, void *stream) {
     if (!w || !w_q || !s_w) return W4A8_ERR_NULL;

@@ -119,21 +119,48 @@ struct Slot {
     bool valid;
 };
 
+// The layers of one launch: layer g owns workgroups [wg_start[g], wg_start[g + 1]), each
+// with rows[g] consecutive rows of it.  NG is the capacity: single-layer launches use NG = 1,
+// which keeps their kernel arguments and prologue as small as before.
+template <int NG>
+struct GroupTab {
+    int G;
+    int wg_start[NG + 1];
+    int rows[NG];
+    LayerDesc L[NG];
+};
+
 // XIN selects the activation input: 0 = prepared int8 x_q and s_x; 1 = fp32 and 2 = bf16
 // raw activations, rotated and quantised in the prologue with the arithmetic of the
 // activation kernel (every workgroup does the same, bit for bit; workgroup 0 also stores
 // x_q and s_x).
-template <int MT, int XIN>
-__global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg) {
+template <int MT, int XIN, int NG>
+__global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt) {
     // The pair table is a static LDS array at a compile-time address, so each lookup is one
     // v_perm for the address and one ds_read_b32; activations and partials follow it in
     // dynamic LDS.
     __shared__ __align__(16) uint32_t lds[kTabWords];
     extern __shared__ uint32_t dyn[];
     const int tid = threadIdx.x;
-    const int64_t K = a.K, N = a.N;
+
+    // this workgroup's layer: the last one whose first workgroup is not after it (selected
+    // with compile-time indices, so the table stays in kernel-argument memory)
+    int gi = 0;
+#pragma unroll
+    for (int q = 1; q < NG; q++) gi = (q < gt.G && (int)blockIdx.x >= gt.wg_start[q]) ? q : gi;
+    LayerDesc L = gt.L[0];
+    int rows_per_wg = gt.rows[0], wg0 = 0;
+#pragma unroll
+    for (int q = 1; q < NG; q++)
+        if (gi == q) {
+            L = gt.L[q];
+            rows_per_wg = gt.rows[q];
+            wg0 = gt.wg_start[q];
+        }
+
+    const int64_t K = a.K, N = L.N;
     const int nblk = (int)(K / kRot);
-    const int64_t r0 = (int64_t)blockIdx.x * rows_per_wg;
+    const int64_t r0 = (int64_t)((int)blockIdx.x - wg0) * rows_per_wg;
     const int nrow = (int)min((int64_t)rows_per_wg, N - r0);
     const int P = (nrow + 1) >> 1;                               // row pairs
     const int units = P * nblk;
@@ -148,9 +175,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     // Workgroup-relative 32-bit offsets into buffer resources bounded by this workgroup's
     // rows: row 2rp+1 past the last row reads as zero and is never stored.
     const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.packed + r0 * rowbytes), (short)0, (int)(nrow * rowbytes), 0x00020000);
+        (void *)(L.packed + r0 * rowbytes), (short)0, (int)(nrow * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.s_rel + r0 * grpbytes), (short)0, (int)(nrow * grpbytes), 0x00020000);
+        (void *)(L.s_rel + r0 * grpbytes), (short)0, (int)(nrow * grpbytes), 0x00020000);
     constexpr int kNT = 2;  // non-temporal: the weights are streamed once per call
 
     // Units in row-major order u = rp * nblk + t; lane group g of wave w takes units
@@ -202,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     // in a register until the final sums), and the activations.  Their loads precede the
     // weight loads in the in-order load counter, so using them does not wait for the
     // weight prefetch.
-    const float sch_mine = tid < nrow ? a.s_ch[r0 + tid] : 0.0f;
+    const float sch_mine = tid < nrow ? L.s_ch[r0 + tid] : 0.0f;
     float sx_all[MT];
     const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
     const int nxc = (int)(MT * (K / 8));
@@ -251,17 +278,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
     // Wave w writes entries 16w .. 16w+15 (high nibble w), each lane its own column.
     float cmax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(a.cb[q]));
+    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(L.cb[q]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
     const float inv = ldexpf(1.0f, -ex);
     {
         static_assert(kThreads / 64 == kLevels, "one wave per high nibble");
         const int w = tid >> 6, lane = tid & 63;
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[w] * inv));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(L.cb[w] * inv));
 #pragma unroll
         for (int lo = 0; lo < kLevels; lo++) {
-            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[lo] * inv)) | (hi << 16);
+            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(L.cb[lo] * inv)) | (hi << 16);
             lds[(16 * w + lo) * 64 + lane] = v;
         }
     }
@@ -384,44 +411,64 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, int rows_per_wg
         const float *pp = part + (m * rows_per_wg + rl) * pstride;
         float acc = 0.0f;
         for (int t = 0; t < nblk; t++) acc += pp[t];
-        const float sch = (i < kThreads && m == 0) ? sch_mine : a.s_ch[r0 + rl];
+        const float sch = (i < kThreads && m == 0) ? sch_mine : L.s_ch[r0 + rl];
         const int64_t r = r0 + rl;
         float sxm = sx_all[0];
 #pragma unroll
         for (int q = 1; q < MT; q++) sxm = (m == q) ? sx_all[q] : sxm;
         const float v = ((acc * sch) * sxm) * cbscale;
         if (a.y_bf16)
-            static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(v);
+            static_cast<uint16_t *>(L.y)[m * N + r] = f32_to_bf16_rne(v);
         else
-            static_cast<float *>(a.y)[m * N + r] = v;
+            static_cast<float *>(L.y)[m * N + r] = v;
     }
 }
 
-template <int MT, int XIN>
-hipError_t launch_mt(const LinearArgs &a, int num_cu, hipStream_t stream) {
+template <int MT, int XIN, int NG>
+hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
+    if (G < 1 || G > NG) return hipErrorInvalidValue;
     const int64_t nblk = a.K / kRot;
     // dynamic part (the 64 KiB table is static): activations, then a [MT][16] scratch for
     // the fused preparation's wave maxima, then the partials
     const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4 + (XIN ? (int64_t)MT * (kThreads / 64) * 4 : 0);
-    int64_t rows = (a.N + num_cu - 1) / num_cu;
-    rows += rows & 1;
     const int64_t dyn_max = kLdsMax - (int64_t)kTabWords * 4;
     const int64_t pstride = nblk | 1;
-    while (rows > 2 && fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) rows = ((rows / 2) + 1) & ~1LL;
-    const int64_t lds = fixed + (int64_t)MT * rows * pstride * 4;
-    if (lds > dyn_max) return hipErrorInvalidValue;
+    int64_t total = 0;
+    for (int g = 0; g < G; g++) total += layers[g].N;
+    // one workgroup per CU in all, shared out in proportion to the layers' rows; a layer's
+    // rows per workgroup are even and small enough for its partials to fit in LDS
+    GroupTab<NG> gt{};
+    gt.G = G;
+    int64_t wg = 0, max_rows = 2;
+    for (int g = 0; g < G; g++) {
+        const int64_t n = layers[g].N;
+        int64_t want = ((int64_t)num_cu * n + total / 2) / total;
+        if (want < 1) want = 1;
+        int64_t rows = (n + want - 1) / want;
+        rows += rows & 1;
+        while (rows > 2 && fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) rows = ((rows / 2) + 1) & ~1LL;
+        if (fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) return hipErrorInvalidValue;
+        gt.wg_start[g] = (int)wg;
+        gt.rows[g] = (int)rows;
+        gt.L[g] = layers[g];
+        wg += (n + rows - 1) / rows;
+        if (rows > max_rows) max_rows = rows;
+    }
+    gt.wg_start[G] = (int)wg;
+    const int64_t lds = fixed + (int64_t)MT * max_rows * pstride * 4;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN, NG>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kLdsMax - kTabWords * 4));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const unsigned grid = (unsigned)((a.N + rows - 1) / rows);
-    hipLaunchKernelGGL((k_gemv<MT, XIN>), dim3(grid), dim3(kThreads), (size_t)lds, stream, a, (int)rows);
+    hipLaunchKernelGGL((k_gemv<MT, XIN, NG>), dim3((unsigned)wg), dim3(kThreads), (size_t)lds, stream, a, gt);
     return hipGetLastError();
 }
+
+LayerDesc single_layer(const LinearArgs &a) { return LayerDesc{a.packed, a.s_rel, a.s_ch, a.cb, a.N, a.y}; }
 
 }  // namespace
 
@@ -431,20 +478,44 @@ bool gemv_fused_supported(int64_t M, int64_t K) {
     return M >= 1 && M <= 2 && K <= (int64_t)64 * kFusedRounds * kRot && gemv_supported(M, K);
 }
 
-hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream) {
+template <int NG>
+hipError_t launch_prepared(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
     switch (a.M) {
-        case 1: return launch_mt<1, 0>(a, num_cu, stream);
-        case 2: return launch_mt<2, 0>(a, num_cu, stream);
-        case 3: return launch_mt<3, 0>(a, num_cu, stream);
-        case 4: return launch_mt<4, 0>(a, num_cu, stream);
+        case 1: return launch_mt<1, 0, NG>(a, layers, G, num_cu, stream);
+        case 2: return launch_mt<2, 0, NG>(a, layers, G, num_cu, stream);
+        case 3: return launch_mt<3, 0, NG>(a, layers, G, num_cu, stream);
+        case 4: return launch_mt<4, 0, NG>(a, layers, G, num_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream) {
-    if (a.M == 1) return a.x_bf16 ? launch_mt<1, 2>(a, num_cu, stream) : launch_mt<1, 1>(a, num_cu, stream);
-    if (a.M == 2) return a.x_bf16 ? launch_mt<2, 2>(a, num_cu, stream) : launch_mt<2, 1>(a, num_cu, stream);
+template <int NG>
+hipError_t launch_fused(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
+    if (a.M == 1)
+        return a.x_bf16 ? launch_mt<1, 2, NG>(a, layers, G, num_cu, stream) : launch_mt<1, 1, NG>(a, layers, G, num_cu, stream);
+    if (a.M == 2)
+        return a.x_bf16 ? launch_mt<2, 2, NG>(a, layers, G, num_cu, stream) : launch_mt<2, 1, NG>(a, layers, G, num_cu, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                             hipStream_t stream) {
+    return launch_prepared<kMaxGroup>(a, layers, G, num_cu, stream);
+}
+
+hipError_t launch_gemv_fused_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                                   hipStream_t stream) {
+    return launch_fused<kMaxGroup>(a, layers, G, num_cu, stream);
+}
+
+hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream) {
+    const LayerDesc l = single_layer(a);
+    return launch_prepared<1>(a, &l, 1, num_cu, stream);
+}
+
+hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream) {
+    const LayerDesc l = single_layer(a);
+    return launch_fused<1>(a, &l, 1, num_cu, stream);
 }
 
 }  // namespace w4a8

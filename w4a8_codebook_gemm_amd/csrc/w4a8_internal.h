@@ -233,6 +233,23 @@ bool gemv_supported(int64_t M, int64_t K);
 bool gemv_fused_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const LinearArgs &a, int num_cu, hipStream_t stream);
 hipError_t launch_gemv_fused(const LinearArgs &a, int num_cu, hipStream_t stream);
+
+// Several layers that read the same activations, run by one GEMV launch: the persistent
+// workgroups are split between the layers in proportion to their rows.  The activation
+// fields of LinearArgs apply to all of them; its layer fields are ignored.
+constexpr int kMaxGroup = 8;
+struct LayerDesc {
+    const int8_t *packed;
+    const uint8_t *s_rel;
+    const float *s_ch;
+    const float *cb;
+    int64_t N;
+    void *y;
+};
+hipError_t launch_gemv_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                             hipStream_t stream);
+hipError_t launch_gemv_fused_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                                   hipStream_t stream);
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
 bool skinny_supported(int64_t M, int64_t N, int64_t K);
