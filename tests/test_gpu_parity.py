@@ -225,7 +225,10 @@ def i8_tight(y, q, xq, sx, rows, toks):
     assert np.all(err <= bound)
 
 
-@pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (128, 256, 128)])
+# 256-token x 192-row tiles: ragged in both directions, several tiles each way, K = 256 (one
+# turn of the four-stage ring)
+@pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (128, 256, 128),
+                                   (385, 1280, 600), (193, 256, 65), (1000, 2048, 513)])
 def test_mfma_i8_parity(w, N, K, M):
     say(f"mfma_i8 N={N} K={K} M={M}")
     y, yr, A, (q, xq, sx) = run_linear(w, w.ALGO_MFMA_I8, N, K, M, n_out=2)

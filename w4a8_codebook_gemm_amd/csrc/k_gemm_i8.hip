@@ -13,28 +13,40 @@
 // The weight rows are the MFMA's N side, so all 16 accumulators of a lane belong to one
 // weight row and share one group scale.  y = acc * s_cb * s_channel[r] * s_x[m].
 //
-// Tile: 128 tokens x 128 rows per 256-thread workgroup (2 x 2 waves of 64 x 64), K steps of
-// 64 (four groups) staged through double-buffered LDS.  Within every 8-wide K chunk the
-// MFMA slot order is (0, 2, 4, 6, 1, 3, 5, 7): the activation tile is stored in that order
-// so that a packed dword decodes with plain nibble masks (low nibbles = even k).
-// Nibble -> int8 decode is a 16-entry byte table in four registers read with v_perm.
+// The fold (one conversion and one fma per partial) is the kernel's bound: it costs more
+// vector-ALU time than the MFMA takes, so everything else is kept off the vector ALU.
+// Tile: 256 tokens x 192 weight rows per 512-thread workgroup, one workgroup per CU.
+// Waves 4 (tokens) x 2 (rows), each 64 x 96 = 2 x 3 MFMA blocks.  K advances in stages of
+// 64 (four groups), double-buffered through LDS, with the global loads four stages ahead in
+// a ring of register stages.  Per stage the workgroup
+//  * copies the int8 activations into [token][64 + 8 pad] rows;
+//  * decodes the packed indices once into int8 weights (byte-permute lookups in a
+//    16-byte cb_i8 table held in registers) in [row][64 + 8 pad] rows;
+//  * decodes the group scales once into fp32 [group][row].
+// The 72-byte rows put the 32 rows one 32-lane phase of an 8-byte fragment read touches on
+// distinct 8-byte bank pairs of the 64 banks.  Tiles are numbered so that each XCD works
+// through a contiguous run, token tiles fastest.
+#include <type_traits>
+
 #include "w4a8_internal.h"
 
 namespace w4a8 {
 namespace {
 
 typedef int int16v __attribute__((ext_vector_type(16)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int kThreads = 256;
-// Padded LDS row strides: 72 B per activation row and 36 B per packed row put the 32 rows
-// that one fragment read touches on distinct banks (LDS has 32 four-byte banks).
-constexpr int kXRow = BK + 8, kPRow = BK / 2 + 4;
+constexpr int BM = 256, BN = 192, BK = 64;
+constexpr int kThreads = 512;
+constexpr int JB = BN / 64;                    // 32-row weight blocks per wave
+constexpr int kPitch = BK + 8;                 // bytes per LDS row
+constexpr int kXStage = BM * kPitch, kBStage = BN * kPitch, kSStage = (BK / kGroup) * BN;
 
 struct CbI8 {
     uint32_t t[4];  // cb_i8[0..15] as bytes
 };
 
+// four 4-bit indices (one per byte) -> the four int8 levels
 __device__ __forceinline__ uint32_t lookup4(const CbI8 &c, uint32_t idx4) {
     const uint32_t sel = idx4 & 0x07070707u;
     const uint32_t lo = __builtin_amdgcn_perm(c.t[1], c.t[0], sel);
@@ -44,28 +56,36 @@ __device__ __forceinline__ uint32_t lookup4(const CbI8 &c, uint32_t idx4) {
     return (mask & hi) | (~mask & lo);
 }
 
-// 8 nibbles (k = 0..7 of a chunk) -> 8 int8 in slot order (0, 2, 4, 6, 1, 3, 5, 7).
-__device__ __forceinline__ long decode8(const CbI8 &c, uint32_t w) {
-    const uint32_t even = lookup4(c, w & 0x0F0F0F0Fu);
-    const uint32_t odd = lookup4(c, (w >> 4) & 0x0F0F0F0Fu);
-    return (long)(((uint64_t)odd << 32) | even);
+// one packed dword (k = 0..7: low nibble of byte b is k = 2b) -> 8 int8 in k order
+__device__ __forceinline__ uint2 decode8(const CbI8 &c, uint32_t w) {
+    const uint32_t even = lookup4(c, w & 0x0F0F0F0Fu);         // k = 0, 2, 4, 6
+    const uint32_t odd = lookup4(c, (w >> 4) & 0x0F0F0F0Fu);   // k = 1, 3, 5, 7
+    return make_uint2(__builtin_amdgcn_perm(odd, even, 0x05010400u), __builtin_amdgcn_perm(odd, even, 0x07030602u));
 }
 
-// Activation bytes x0..x7 -> slot order (x0, x2, x4, x6, x1, x3, x5, x7).
-__device__ __forceinline__ uint2 slot_order(uint32_t d0, uint32_t d1) {
-    return make_uint2(__builtin_amdgcn_perm(d1, d0, 0x06040200u),
-                      __builtin_amdgcn_perm(d1, d0, 0x07050301u));
-}
+struct Stage {
+    uint4 x0, x1;   // 32 activation bytes of token xr
+    uint4 p;        // 32 packed indices of weight row pr (two groups)
+    uint32_t s;     // the four e4m3 group scales of weight row sr (threads < BN)
+};
 
-__global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
-    __shared__ __align__(16) uint8_t xs[2][BM * kXRow];
-    __shared__ __align__(16) uint8_t ps[2][BN * kPRow];
-    __shared__ __align__(16) uint8_t ss[2][BN * BK / kGroup];
+template <int J>
+using IC = std::integral_constant<int, J>;
+
+__global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a, int tiles_m, int tiles) {
+    __shared__ __align__(16) int8_t xs[2][kXStage];
+    __shared__ __align__(16) int8_t bs[2][kBStage];
+    __shared__ __align__(16) float ss[2][kSStage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+
+    // consecutive workgroups go to consecutive XCDs: XCD x takes the contiguous tile run
+    // starting at x*q + min(x, rem)
+    const int b = blockIdx.x, q = tiles / 8, rem = tiles % 8, xcd = b % 8, slot = b / 8;
+    const int t = xcd * q + min(xcd, rem) + slot;
+    const int64_t m0 = (int64_t)(t % tiles_m) * BM, n0 = (int64_t)(t / tiles_m) * BN;
 
     // int8 form of the codebook (same fp32 arithmetic at every thread)
     float cmax = 0.0f;
@@ -77,101 +97,135 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
     for (int w = 0; w < 4; w++) {
         uint32_t v = 0;
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int q = (s_cb > 0.0f) ? (int)rintf(a.cb[4 * w + b] / s_cb) : 0;
-            v |= ((uint32_t)q & 0xFFu) << (8 * b);
+        for (int bb = 0; bb < 4; bb++) {
+            const int qv = (s_cb > 0.0f) ? (int)rintf(a.cb[4 * w + bb] / s_cb) : 0;
+            v |= ((uint32_t)qv & 0xFFu) << (8 * bb);
         }
         cbt.t[w] = v;
     }
 
-    // global -> register staging assignment (rows past M or N read row 0 and are zeroed)
-    const int xr = tid >> 1, xh = tid & 1;      // x: row xr, 32 bytes at 32*xh
-    const int pr = tid >> 1, ph = tid & 1;      // packed: row pr, 16 bytes at 16*ph
-    const bool xvalid = m0 + xr < M, pvalid = n0 + pr < N;
-    const bool svalid = tid < BN && n0 + tid < N;
-    const uint4 *xsrc = reinterpret_cast<const uint4 *>(a.x_q + (xvalid ? (m0 + xr) * K : 0) + 32 * xh);
-    const uint4 *psrc = reinterpret_cast<const uint4 *>(a.packed + (pvalid ? (n0 + pr) * (K / 2) : 0) + 16 * ph);
-    const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(a.s_rel + (svalid ? (n0 + tid) * (K / kGroup) : 0));
-    const uint32_t xmask = xvalid ? 0xFFFFFFFFu : 0u, pmask = pvalid ? 0xFFFFFFFFu : 0u;
-    const uint32_t smask = svalid ? 0xFFFFFFFFu : 0u;
-    uint8_t *xdst0 = &xs[0][xr * kXRow + 32 * xh];
-    uint8_t *pdst0 = &ps[0][pr * kPRow + 16 * ph];
-    uint8_t *sdst0 = &ss[0][(tid & (BN - 1)) * 4];
-    constexpr int xbuf = BM * kXRow, pbuf = BN * kPRow, sbuf = BN * BK / kGroup;
+    // ---- staging roles: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight row pr,
+    // weights [32 ph, 32 ph + 32) (two groups); group scales of row sr.  Rows past M or N
+    // re-read the last valid row: they feed only outputs that are never stored.  Threads
+    // past 2 BN (packed) or BN (scales) load like the last row's but store nothing.
+    const int xr = tid >> 1, xh = tid & 1;
+    const int pr0 = tid >> 1, ph = tid & 1;
+    const bool pdec = pr0 < BN;                    // wave-uniform: 2 BN is a multiple of 64
+    const int pr = pdec ? pr0 : BN - 1;
+    const bool sdec = tid < BN;                    // wave-uniform: BN is a multiple of 64
+    const int sr = sdec ? tid : BN - 1;
+    const int8_t *xp = a.x_q + min<int64_t>(m0 + xr, M - 1) * K + 32 * xh;
+    const int8_t *pp = a.packed + min<int64_t>(n0 + pr, N - 1) * (K / 2) + 16 * ph;
+    // a row's group scales start 16-byte aligned (K / 16 is a multiple of 16); one dword
+    // holds the stage's four
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(a.s_rel + min<int64_t>(n0 + sr, N - 1) * (K / kGroup));
+    const int nk = (int)(K / BK);
 
-    float acc[2][2][16];
+    // every stage's loads are issued unconditionally (stages past the end re-read the last
+    // one) so that the in-order load counter lets a decode wait for its own stage only
+    auto gload = [&](int kt, Stage &st) {
+        const int k = kt < nk ? kt : nk - 1;
+        st.x0 = *reinterpret_cast<const uint4 *>(xp + (int64_t)k * BK);
+        st.x1 = *reinterpret_cast<const uint4 *>(xp + (int64_t)k * BK + 16);
+        st.p = *reinterpret_cast<const uint4 *>(pp + (int64_t)k * (BK / 2));
+        st.s = sp[k];
+    };
+    int8_t *const xdst = &xs[0][xr * kPitch + 32 * xh];
+    int8_t *const bdst = &bs[0][pr * kPitch + 32 * ph];
+    auto lstore = [&](auto bufc, const Stage &st) {
+        constexpr int buf = decltype(bufc)::value;
+        // 72-byte rows: 8-byte stores
+        uint2 *dx = reinterpret_cast<uint2 *>(xdst + buf * kXStage);
+        dx[0] = make_uint2(st.x0.x, st.x0.y);
+        dx[1] = make_uint2(st.x0.z, st.x0.w);
+        dx[2] = make_uint2(st.x1.x, st.x1.y);
+        dx[3] = make_uint2(st.x1.z, st.x1.w);
+        if (pdec) {
+            uint2 *db = reinterpret_cast<uint2 *>(bdst + buf * kBStage);
+            db[0] = decode8(cbt, st.p.x);
+            db[1] = decode8(cbt, st.p.y);
+            db[2] = decode8(cbt, st.p.z);
+            db[3] = decode8(cbt, st.p.w);
+        }
+        if (sdec) {
+            // gfx950's v_cvt_f32_fp8 decodes OCP E4M3FN exactly
+            float *dsc = &ss[buf][sr];
+            dsc[0 * BN] = __builtin_amdgcn_cvt_f32_fp8((int)st.s, 0);
+            dsc[1 * BN] = __builtin_amdgcn_cvt_f32_fp8((int)st.s, 1);
+            dsc[2 * BN] = __builtin_amdgcn_cvt_f32_fp8((int)st.s, 2);
+            dsc[3 * BN] = __builtin_amdgcn_cvt_f32_fp8((int)st.s, 3);
+        }
+    };
+
+    float16_t acc[2][JB];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < JB; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-    const int nk = (int)(K / BK);
-    uint4 rx0 = xsrc[0], rx1 = xsrc[1], rp = psrc[0];
-    uint32_t rs = ssrc[0];
-#define W4A8_STAGE_STORE(buf)                                                                   \
-    do {                                                                                        \
-        const uint2 o0 = slot_order(rx0.x & xmask, rx0.y & xmask);                              \
-        const uint2 o1 = slot_order(rx0.z & xmask, rx0.w & xmask);                              \
-        const uint2 o2 = slot_order(rx1.x & xmask, rx1.y & xmask);                              \
-        const uint2 o3 = slot_order(rx1.z & xmask, rx1.w & xmask);                              \
-        uint2 *dx = reinterpret_cast<uint2 *>(xdst0 + (buf) * xbuf);  /* 8-B aligned rows */   \
-        dx[0] = o0; dx[1] = o1; dx[2] = o2; dx[3] = o3;                                         \
-        uint32_t *dp = reinterpret_cast<uint32_t *>(pdst0 + (buf) * pbuf); /* 4-B aligned */    \
-        dp[0] = rp.x & pmask; dp[1] = rp.y & pmask; dp[2] = rp.z & pmask; dp[3] = rp.w & pmask;  \
-        if (tid < BN) *reinterpret_cast<uint32_t *>(sdst0 + (buf) * sbuf) = rs & smask;          \
-    } while (0)
-    W4A8_STAGE_STORE(0);
+    Stage R0, R1, R2, R3;
+    gload(0, R0);
+    gload(1, R1);
+    gload(2, R2);
+    gload(3, R3);
+    lstore(IC<0>{}, R0);
     __syncthreads();
+
     const int half = lane >> 5, l32 = lane & 31;
-    for (int kt = 0; kt < nk; kt++) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            const int64_t k1 = (int64_t)(kt + 1) * BK;
-            rx0 = xsrc[k1 / 16];
-            rx1 = xsrc[k1 / 16 + 1];
-            rp = psrc[k1 / 32];
-            rs = ssrc[k1 / 64];
-        }
-        // rolled on purpose: each group's four MFMA results are folded before the next
-        // group's MFMAs issue, so only 64 partials are live at a time
+    const int8_t *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 8 * half];
+    const int8_t *const brd = &bs[0][(wn * (BN / 2) + l32) * kPitch + 8 * half];
+    const float *const srd = &ss[0][wn * (BN / 2) + l32];
+
+    auto mfmas = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        // rolled on purpose: each group's partials are folded before the next group's
+        // MFMAs issue, so only one group's partials are live at a time
 #pragma unroll 1
         for (int g = 0; g < BK / kGroup; g++) {
-            long A[2], B[2];
-            float s[2];
+            long A[2], B[JB];
+            float s[JB];
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++) {
-                const int row = wm * 64 + ib * 32 + l32;
-                A[ib] = *reinterpret_cast<const long *>(&xs[buf][row * kXRow + g * kGroup + 8 * half]);
-            }
+            for (int ib = 0; ib < 2; ib++)
+                A[ib] = *reinterpret_cast<const long *>(xrd + buf * kXStage + ib * 32 * kPitch + g * kGroup);
 #pragma unroll
-            for (int jb = 0; jb < 2; jb++) {
-                const int row = wn * 64 + jb * 32 + l32;
-                const uint32_t w = *reinterpret_cast<const uint32_t *>(&ps[buf][row * kPRow + g * 8 + 4 * half]);
-                B[jb] = decode8(cbt, w);
-                s[jb] = e4m3_to_f32(ss[buf][row * 4 + g]);
+            for (int jb = 0; jb < JB; jb++) {
+                B[jb] = *reinterpret_cast<const long *>(brd + buf * kBStage + jb * 32 * kPitch + g * kGroup);
+                s[jb] = srd[buf * kSStage + g * BN + jb * 32];
             }
 #pragma unroll
             for (int ib = 0; ib < 2; ib++)
 #pragma unroll
-                for (int jb = 0; jb < 2; jb++) {
+                for (int jb = 0; jb < JB; jb++) {
                     const int16v zero = {};
                     const int16v P = __builtin_amdgcn_mfma_i32_32x32x16_i8(A[ib], B[jb], zero, 0, 0, 0);
 #pragma unroll
                     for (int v = 0; v < 16; v++) acc[ib][jb][v] = fmaf(s[jb], (float)P[v], acc[ib][jb][v]);
                 }
         }
-        if (kt + 1 < nk) W4A8_STAGE_STORE(buf ^ 1);
+    };
+    // step s (ring slot J = s % 4): its stage is in LDS buffer J % 2; the slot reloads stage
+    // s + 4; stage s + 1 (loaded three steps ago) is staged into the other buffer
+    auto step = [&](int s, auto jc, Stage &Rcur, Stage &Rnext) {
+        constexpr int J = decltype(jc)::value;
+        gload(s + 4, Rcur);
+        lstore(IC<(J + 1) % 2>{}, Rnext);
+        mfmas(IC<J % 2>{});
         __syncthreads();
+    };
+    // nk = K / 64 is a multiple of 4 (K is a multiple of 256): whole ring turns only
+    for (int s = 0; s < nk; s += 4) {
+        step(s, IC<0>{}, R0, R1);
+        step(s + 1, IC<1>{}, R1, R2);
+        step(s + 2, IC<2>{}, R2, R3);
+        step(s + 3, IC<3>{}, R3, R0);
     }
 
-#undef W4A8_STAGE_STORE
-
-    // epilogue: lane holds column j = l32 (weight row) and rows i = 8(v/4) + 4 half + v%4
+    // ---- epilogue: lane holds column j = l32 (weight row), tokens 8(v/4) + 4 half + v%4
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++) {
-        const int64_t r = n0 + wn * 64 + jb * 32 + l32;
+    for (int jb = 0; jb < JB; jb++) {
+        const int64_t r = n0 + wn * (BN / 2) + jb * 32 + l32;
         if (r >= N) continue;
         const float rs_ = a.s_ch[r] * s_cb;
 #pragma unroll
@@ -193,8 +247,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_i8(LinearArgs a) {
 }  // namespace
 
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream) {
-    dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-    hipLaunchKernelGGL(k_gemm_i8, grid, dim3(kThreads), 0, stream, a);
+    const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+    hipLaunchKernelGGL(k_gemm_i8, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, a, (int)tm,
+                       (int)(tm * tn));
     return hipGetLastError();
 }
 
