@@ -19,11 +19,14 @@
 // token.  A wave folds its lane sums with a butterfly when it leaves a row and adds them to
 // the row's int32 accumulator in LDS (integer adds: the result does not depend on order).
 //
-// Kernel W2 (prefill): int8 MFMA GEMM, v_mfma_i32_32x32x32_i8, 128 x 128 tiles per
-// 256-thread workgroup (2 x 2 waves of 64 x 64), 128-byte K stages double-buffered through
-// LDS, int32 accumulation over all of K, scales applied once in the epilogue.  Tiles are
+// Kernel W2 (prefill): int8 MFMA GEMM, v_mfma_i32_32x32x32_i8, 256 tokens x 192 rows per
+// 512-thread workgroup (4 x 2 waves of 64 x 96), one workgroup per CU, 64-byte K stages
+// double-buffered through LDS with the global loads four stages ahead in a ring of register
+// stages, int32 accumulation over all of K, scales applied once in the epilogue.  Tiles are
 // numbered so that each XCD works through a contiguous run of them, token tiles fastest,
 // which keeps a weight tile's reuse within one XCD's L2.
+#include <type_traits>
+
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -153,103 +156,135 @@ __global__ __launch_bounds__(kGvThreads) void k_w8_gemv(W8Args a) {
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 
-constexpr int GB = 128;             // tile edge (tokens and weight rows)
-constexpr int GK = 128;             // K bytes per stage
-constexpr int kGmThreads = 256;
-// 144-byte LDS rows: the 16 rows one 16-lane phase of a fragment read touches start at
-// distinct multiples of 16 bytes modulo 256, i.e. on disjoint bank quads of the 64 banks
+constexpr int GM = 256, GN = 192, GK = 64;  // tile: tokens x weight rows x K bytes per stage
+constexpr int kGmThreads = 512;
+constexpr int GJB = GN / 64;                // 32-row weight blocks per wave
+// 80-byte LDS rows: the 16 rows one 16-lane phase of a 16-byte fragment read touches start
+// at distinct multiples of 16 bytes modulo 256, i.e. on disjoint bank quads of the 64 banks
 constexpr int kPitch = GK + 16;
+constexpr int kXSt = GM * kPitch, kWSt = GN * kPitch;
 
-__global__ __launch_bounds__(kGmThreads) void k_w8_gemm(W8Args a, int tiles_m, int tiles) {
-    __shared__ __align__(16) int8_t xs[2][GB * kPitch];
-    __shared__ __align__(16) int8_t ws[2][GB * kPitch];
+struct GStage {
+    int4v x0, x1;   // 32 activation bytes of token xr
+    int4v w0, w1;   // 16 weight bytes of rows wr and wr + 128 (the latter for threads < 256)
+};
+
+template <int J>
+using GIC = std::integral_constant<int, J>;
+
+// two waves per SIMD: the accumulators and the register ring need up to 256 registers
+__global__ __launch_bounds__(kGmThreads, 1) void k_w8_gemm(W8Args a, int tiles_m, int tiles) {
+    __shared__ __align__(16) int8_t xs[2][kXSt];
+    __shared__ __align__(16) int8_t ws[2][kWSt];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
     const int64_t M = a.M, N = a.N, K = a.K;
 
     // consecutive workgroups go to consecutive XCDs: give XCD x the contiguous tile run
     // [x*q + min(x, rem), ...) so that neighbouring tiles share an L2
     const int b = blockIdx.x, q = tiles / 8, rem = tiles % 8, xcd = b % 8, slot = b / 8;
     const int t = xcd * q + min(xcd, rem) + slot;
-    const int64_t m0 = (int64_t)(t % tiles_m) * GB, n0 = (int64_t)(t / tiles_m) * GB;
+    const int64_t m0 = (int64_t)(t % tiles_m) * GM, n0 = (int64_t)(t / tiles_m) * GN;
 
-    // staging: thread -> rows sr + 32 i, bytes [sc, sc + 16) of the stage.  Rows past M or N
-    // re-read the last valid row; they feed only outputs that are never stored.
-    const int sr = tid >> 3, sc = (tid & 7) * 16;
-    const int8_t *xrow[4], *wrow[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int64_t mr = m0 + sr + 32 * i, nr = n0 + sr + 32 * i;
-        xrow[i] = a.x_q + (mr < M ? mr : M - 1) * K + sc;
-        wrow[i] = a.w_q + (nr < N ? nr : N - 1) * K + sc;
-    }
-    uint4 rx[4], rw[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        rx[i] = *reinterpret_cast<const uint4 *>(xrow[i]);
-        rw[i] = *reinterpret_cast<const uint4 *>(wrow[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        *reinterpret_cast<uint4 *>(&xs[0][(sr + 32 * i) * kPitch + sc]) = rx[i];
-        *reinterpret_cast<uint4 *>(&ws[0][(sr + 32 * i) * kPitch + sc]) = rw[i];
-    }
-    __syncthreads();
+    // staging: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight rows wr and wr + 128,
+    // bytes [16 wq, 16 wq + 16) (rows 128 .. 191 by threads < 256).  Rows past M or N re-read
+    // the last valid row: they feed only outputs that are never stored.  Threads past 256
+    // load a second row like row 191's but store nothing.
+    static_assert(GN > 128 && GN <= 256 && kGmThreads == 512, "weight staging covers 128 + (GN - 128) rows");
+    const int xr = tid >> 1, xh = tid & 1;
+    const int wr = tid >> 2, wq = tid & 3;
+    const bool w1st = wr < GN - 128;               // wave-uniform: 4 (GN - 128) is a multiple of 64
+    const int8_t *xp = a.x_q + min<int64_t>(m0 + xr, M - 1) * K + 32 * xh;
+    const int8_t *wp0 = a.w_q + min<int64_t>(n0 + wr, N - 1) * K + 16 * wq;
+    const int8_t *wp1 = a.w_q + min<int64_t>(n0 + (w1st ? 128 + wr : GN - 1), N - 1) * K + 16 * wq;
+    const int nk = (int)(K / GK);
 
-    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, hk = (lane >> 5) * 16;
-    int16v acc[2][2];
+    // every stage's loads are issued unconditionally (stages past the end re-read the last
+    // one) so that the in-order load counter lets a store wait for its own stage only
+    auto gload = [&](int kt, GStage &st) {
+        const int64_t k = (int64_t)(kt < nk ? kt : nk - 1) * GK;
+        st.x0 = *reinterpret_cast<const int4v *>(xp + k);
+        st.x1 = *reinterpret_cast<const int4v *>(xp + k + 16);
+        st.w0 = *reinterpret_cast<const int4v *>(wp0 + k);
+        st.w1 = *reinterpret_cast<const int4v *>(wp1 + k);
+    };
+    int8_t *const xdst = &xs[0][xr * kPitch + 32 * xh];
+    int8_t *const wdst = &ws[0][wr * kPitch + 16 * wq];   // row wr; row wr + 128 is 128 rows on
+    auto lstore = [&](auto bufc, const GStage &st) {
+        constexpr int buf = decltype(bufc)::value;
+        int4v *dx = reinterpret_cast<int4v *>(xdst + buf * kXSt);
+        dx[0] = st.x0;
+        dx[1] = st.x1;
+        *reinterpret_cast<int4v *>(wdst + buf * kWSt) = st.w0;
+        if (w1st) *reinterpret_cast<int4v *>(wdst + buf * kWSt + 128 * kPitch) = st.w1;
+    };
+
+    int16v acc[2][GJB];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = int16v{};
+        for (int j = 0; j < GJB; j++) acc[i][j] = int16v{};
 
-    const int nk = (int)(K / GK);
-    for (int kt = 0; kt < nk; kt++) {
-        const int buf = kt & 1;
-        // the next stage (the last stage again on the last step: loaded and stored into the
-        // idle buffer, never read), unconditional so the staging stays in registers
-        const int64_t k1 = (int64_t)(kt + 1 < nk ? kt + 1 : kt) * GK;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            rx[i] = *reinterpret_cast<const uint4 *>(xrow[i] + k1);
-            rw[i] = *reinterpret_cast<const uint4 *>(wrow[i] + k1);
-        }
+    GStage R0, R1, R2, R3;
+    gload(0, R0);
+    gload(1, R1);
+    gload(2, R2);
+    gload(3, R3);
+    lstore(GIC<0>{}, R0);
+    __syncthreads();
+
+    const int half = lane >> 5, l32 = lane & 31;
+    const int8_t *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 16 * half];
+    const int8_t *const wrd = &ws[0][(wn * (GN / 2) + l32) * kPitch + 16 * half];
+    auto mfmas = [&](auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
 #pragma unroll
         for (int s = 0; s < GK / 32; s++) {
-            int4v A[2], B[2];
+            int4v A[2], B[GJB];
 #pragma unroll
             for (int ib = 0; ib < 2; ib++)
-                A[ib] = *reinterpret_cast<const int4v *>(&xs[buf][(wm * 64 + ib * 32 + l32) * kPitch + s * 32 + hk]);
+                A[ib] = *reinterpret_cast<const int4v *>(xrd + buf * kXSt + ib * 32 * kPitch + s * 32);
 #pragma unroll
-            for (int jb = 0; jb < 2; jb++)
-                B[jb] = *reinterpret_cast<const int4v *>(&ws[buf][(wn * 64 + jb * 32 + l32) * kPitch + s * 32 + hk]);
+            for (int jb = 0; jb < GJB; jb++)
+                B[jb] = *reinterpret_cast<const int4v *>(wrd + buf * kWSt + jb * 32 * kPitch + s * 32);
             // A and B lanes carry the same 16 k of the 32-wide step, so the product is the
             // full sum over the step whatever order the unit takes them in
 #pragma unroll
             for (int ib = 0; ib < 2; ib++)
 #pragma unroll
-                for (int jb = 0; jb < 2; jb++)
+                for (int jb = 0; jb < GJB; jb++)
                     acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            *reinterpret_cast<uint4 *>(&xs[buf ^ 1][(sr + 32 * i) * kPitch + sc]) = rx[i];
-            *reinterpret_cast<uint4 *>(&ws[buf ^ 1][(sr + 32 * i) * kPitch + sc]) = rw[i];
-        }
+    };
+    // step s (ring slot J = s % 4): its stage is in LDS buffer J % 2; the slot reloads stage
+    // s + 4; stage s + 1 (loaded three steps ago) is staged into the other buffer
+    auto step = [&](int s, auto jc, GStage &Rcur, GStage &Rnext) {
+        constexpr int J = decltype(jc)::value;
+        gload(s + 4, Rcur);
+        lstore(GIC<(J + 1) % 2>{}, Rnext);
+        mfmas(GIC<J % 2>{});
         __syncthreads();
+    };
+    // nk = K / 64 is a multiple of 4 (K is a multiple of 256): whole ring turns only
+    for (int s = 0; s < nk; s += 4) {
+        step(s, GIC<0>{}, R0, R1);
+        step(s + 1, GIC<1>{}, R1, R2);
+        step(s + 2, GIC<2>{}, R2, R3);
+        step(s + 3, GIC<3>{}, R3, R0);
     }
 
     // lane holds weight row j = l32 of each 32 x 32 block and tokens 8(v/4) + 4 half + v%4
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++) {
-        const int64_t r = n0 + wn * 64 + jb * 32 + l32;
+    for (int jb = 0; jb < GJB; jb++) {
+        const int64_t r = n0 + wn * (GN / 2) + jb * 32 + l32;
         if (r >= N) continue;
         const float sw = a.s_w[r];
 #pragma unroll
         for (int ib = 0; ib < 2; ib++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int64_t m = m0 + wm * 64 + ib * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t m = m0 + wm * 64 + ib * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
                 if (m < M) {
                     const float val = ((float)acc[ib][jb][v] * sw) * a.s_x[m];
                     if (a.y_bf16)
@@ -279,7 +314,7 @@ hipError_t launch_w8_gemv(const W8Args &a, int num_cu, hipStream_t stream) {
 }
 
 hipError_t launch_w8_gemm(const W8Args &a, hipStream_t stream) {
-    const int64_t tm = (a.M + GB - 1) / GB, tn = (a.N + GB - 1) / GB;
+    const int64_t tm = (a.M + GM - 1) / GM, tn = (a.N + GN - 1) / GN;
     hipLaunchKernelGGL(k_w8_gemm, dim3((unsigned)(tm * tn)), dim3(kGmThreads), 0, stream, a, (int)tm,
                        (int)(tm * tn));
     return hipGetLastError();
