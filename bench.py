@@ -456,6 +456,56 @@ def w8a8(w, torch, S, shapes, w4_gemv, w4_unfused_us, w4_prefill, M=2048):
     if w4_prefill:
         out["prefill"]["w4a8_best_tops"] = max(w4_prefill["mfma_i8"]["tops"], w4_prefill["mfma_f16"]["tops"])
     del layers
+    torch.cuda.empty_cache()
+    out["model"] = w8a8_model(w, torch, S)
+    return out
+
+
+def w8a8_model(w, torch, S, tokens=10):
+    """The 62-layer decoder of `model` with W8A8 weights: one token = prepare each input once,
+    then one W8A8 GEMV per projection (496 launches), weights read once per token."""
+    base = {}
+    for sh in (S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE):
+        W = torch.from_numpy(S.weights(*sh, seed=0)).cuda()
+        base[sh] = w.w8a8_quantize_weight(W)
+        torch.cuda.synchronize()
+        del W
+    clone = lambda L: w.W8Linear(L.w_q.clone(), L.s_w.clone())
+    layers = [dict(attn=[clone(base[S.ATTN_SQUARE]) for _ in range(5)], gate=clone(base[S.MLP_GATE_UP]),
+                   up=clone(base[S.MLP_GATE_UP]), down=clone(base[S.MLP_DOWN])) for _ in range(MODEL_LAYERS)]
+    torch.cuda.synchronize()
+    per_layer = sum(n * k + 4 * n for (n, k) in [S.ATTN_SQUARE] * 5 + [S.MLP_GATE_UP] * 2 + [S.MLP_DOWN])
+    total = per_layer * MODEL_LAYERS
+    d, f = S.ATTN_SQUARE[1], S.MLP_DOWN[1]
+    xs = {key: torch.from_numpy(S.activations(1, k, seed=i)).cuda()
+          for i, (key, k) in enumerate((("attn_in", d), ("attn_out", d), ("mlp_in", d), ("mlp_hid", f)))}
+    xq = {key: (torch.empty((1, v.shape[1]), dtype=torch.int8, device="cuda"),
+                torch.empty((1,), dtype=torch.float32, device="cuda")) for key, v in xs.items()}
+    y5, y17 = (torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (d, S.MLP_GATE_UP[0]))
+
+    def token():
+        for L in layers:
+            w.prepare_activation(xs["attn_in"], out=xq["attn_in"])
+            for j in range(4):
+                w.w8a8_linear(*xq["attn_in"], L["attn"][j], out=y5)
+            w.prepare_activation(xs["attn_out"], out=xq["attn_out"])
+            w.w8a8_linear(*xq["attn_out"], L["attn"][4], out=y5)
+            w.prepare_activation(xs["mlp_in"], out=xq["mlp_in"])
+            w.w8a8_linear(*xq["mlp_in"], L["gate"], out=y17)
+            w.w8a8_linear(*xq["mlp_in"], L["up"], out=y17)
+            w.prepare_activation(xs["mlp_hid"], out=xq["mlp_hid"])
+            w.w8a8_linear(*xq["mlp_hid"], L["down"], out=y5)
+
+    g = make_graph(torch, token)
+    g.replay()
+    torch.cuda.synchronize()
+    t = time_graph(torch, g, tokens)
+    log(f"W8A8 model: {MODEL_LAYERS} layers, {total / 1e9:.2f} GB, {t * 1e3:.3f} ms/token, {1 / t:.1f} tokens/s, "
+        f"{total / t / 1e9:.1f} GB/s")
+    out = dict(weight_bytes=total, launches_per_token=12 * MODEL_LAYERS, ms_per_token=round(t * 1e3, 4),
+               tokens_per_s=round(1 / t, 1), weight_gbs=round(total / t / 1e9, 1),
+               hbm_bound_tokens_per_s=round(HBM_PEAK_GBS * 1e9 / total, 1))
+    del layers, base, g
     return out
 
 
