@@ -29,9 +29,12 @@
 //    block parity so that the two groups served together cover all 64 LDS banks.
 //  * Each group's two-element dot products are summed in fp32, scaled by the decoded e4m3
 //    group scale, reduced over the 8 lanes with xor shuffles, and written to an LDS
-//    partial per (row, block) (odd row stride: conflict-free); one thread per row then
-//    sums its partials in block order and applies s_channel (loaded at kernel start), s_x
+//    partial per (row, block) (odd row stride: conflict-free); eight lanes per row then
+//    sum its partials in a fixed order and apply s_channel (loaded at kernel start), s_x
 //    and the codebook's power-of-two scale.  No atomics: the result is deterministic.
+//  * Start-up: every small operand (codebook, row scales, activations) is requested before
+//    the first weight loads; a request issued behind them would wait for the whole first
+//    wave of weight traffic to drain from HBM before the table could be built.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -229,7 +232,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // in a register until the final sums), and the activations.  Their loads precede the
     // weight loads in the in-order load counter, so using them does not wait for the
     // weight prefetch.
-    const float sch_mine = tid < nrow ? L.s_ch[r0 + tid] : 0.0f;
+    const float sch_mine = (tid >> 3) < nrow ? L.s_ch[r0 + (tid >> 3)] : 0.0f;  // row of the first final-sum pass
+    // The codebook (four 16-byte loads, the same line for every lane) and this wave's
+    // high-nibble level, loaded with the other small operands before the weight stream: a
+    // load issued behind the stream's first requests waits for them to drain from HBM.
+    const __amdgpu_buffer_rsrc_t rs_cb = __builtin_amdgcn_make_buffer_rsrc((void *)L.cb, (short)0, kLevels * 4, 0x00020000);
+    float cbv[kLevels];
+#pragma unroll
+    for (int q = 0; q < kLevels / 4; q++) {
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs_cb, 16 * q, 0, 0);
+        cbv[4 * q] = __uint_as_float(c.x); cbv[4 * q + 1] = __uint_as_float(c.y);
+        cbv[4 * q + 2] = __uint_as_float(c.z); cbv[4 * q + 3] = __uint_as_float(c.w);
+    }
+    const float cb_hi = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_cb, 4 * (tid >> 6), 0, 0));
     float sx_all[MT];
     const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
     const int nxc = (int)(MT * (K / 8));
@@ -262,7 +277,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     }
 
     // A ring of kDepth units in flight per lane group; the first loads are issued before
-    // the prologue so their HBM latency overlaps the table build.
+    // the prologue so their HBM latency overlaps the table build.  The scheduling barrier
+    // keeps every small operand's load ahead of them.
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int kDepth = depth<MT>();
     Slot cur[kDepth];
     u32x4 pa[kDepth], pb[kDepth];
@@ -278,17 +295,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // Wave w writes entries 16w .. 16w+15 (high nibble w), each lane its own column.
     float cmax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(L.cb[q]));
+    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(cbv[q]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
     const float inv = ldexpf(1.0f, -ex);
     {
         static_assert(kThreads / 64 == kLevels, "one wave per high nibble");
         const int w = tid >> 6, lane = tid & 63;
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(L.cb[w] * inv));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(cb_hi * inv));
 #pragma unroll
         for (int lo = 0; lo < kLevels; lo++) {
-            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(L.cb[lo] * inv)) | (hi << 16);
+            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(cbv[lo] * inv)) | (hi << 16);
             lds[(16 * w + lo) * 64 + lane] = v;
         }
     }
@@ -404,23 +421,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     }
     __syncthreads();
 
-    // one thread per (token, row): sum the row's block partials in block order
+    // eight lanes per (token, row): lane e sums the row's block partials e, e + 8, ... in
+    // block order, then the eight sums are added pairwise in a fixed pattern (deterministic,
+    // and the same for every launch shape of the layer)
     const float cbscale = ldexpf(1.0f, ex);
-    for (int i = tid; i < MT * nrow; i += kThreads) {
-        const int m = i / nrow, rl = i - m * nrow;
+    for (int i = tid >> 3; i < MT * nrow; i += kThreads / 8) {
+        const int m = MT == 1 ? 0 : i / nrow, rl = i - m * nrow;
         const float *pp = part + (m * rows_per_wg + rl) * pstride;
         float acc = 0.0f;
-        for (int t = 0; t < nblk; t++) acc += pp[t];
-        const float sch = (i < kThreads && m == 0) ? sch_mine : L.s_ch[r0 + rl];
-        const int64_t r = r0 + rl;
-        float sxm = sx_all[0];
+        for (int t = j; t < nblk; t += 8) acc += pp[t];
+        acc = sum8_to_leader(acc);
+        if (j == 0) {
+            const float sch = (i < kThreads / 8 && m == 0) ? sch_mine : L.s_ch[r0 + rl];
+            const int64_t r = r0 + rl;
+            float sxm = sx_all[0];
 #pragma unroll
-        for (int q = 1; q < MT; q++) sxm = (m == q) ? sx_all[q] : sxm;
-        const float v = ((acc * sch) * sxm) * cbscale;
-        if (a.y_bf16)
-            static_cast<uint16_t *>(L.y)[m * N + r] = f32_to_bf16_rne(v);
-        else
-            static_cast<float *>(L.y)[m * N + r] = v;
+            for (int q = 1; q < MT; q++) sxm = (m == q) ? sx_all[q] : sxm;
+            const float v = ((acc * sch) * sxm) * cbscale;
+            if (a.y_bf16)
+                static_cast<uint16_t *>(L.y)[m * N + r] = f32_to_bf16_rne(v);
+            else
+                static_cast<float *>(L.y)[m * N + r] = v;
+        }
     }
 }
 
