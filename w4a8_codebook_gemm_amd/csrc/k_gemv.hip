@@ -114,6 +114,40 @@ __device__ __forceinline__ float sum8_to_leader(float v) {
     return v;
 }
 
+// Maximum over the 64 lanes of a wave of non-negative values (exact in any order): DPP
+// within each 16-lane row, then the four row maxima read as scalars.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));  // row_ror:4
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));  // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The int8 activations of sixteen rotated values as clamped integers in fp32, with the
+// arithmetic of quant16_auto (bit-identical results): the exactly corrected reciprocal
+// when s >= kQuantFastMin, IEEE division otherwise, all zero when the token is zero.
+__device__ __forceinline__ void quant16_values(const float v[16], float s, float r, bool nonzero, float q[16]) {
+    const bool fast = s >= kQuantFastMin;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        float t;
+        if (fast) {
+            const float q0 = v[i] * r;
+            const float e = fmaf(-q0, s, v[i]);
+            t = rintf(fmaf(e, r, q0));
+        } else {
+            t = rintf(v[i] / s);
+        }
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        q[i] = nonzero ? t : 0.0f;
+    }
+}
+
 // One ring slot: buffer offsets of a unit for this lane, where its activations and partial
 // live in LDS, and whether it exists.
 struct Slot {
@@ -344,8 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
                     for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(xr[m][r][q]));
                 }
             }
-#pragma unroll
-            for (int sh = 32; sh > 0; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+            amax = wave_max_nonneg(amax);
             if (lane64 == 0) red[m * (kThreads / 64) + wave64] = amax;
         }
         __syncthreads();
@@ -362,17 +395,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
             for (int r = 0; r < kFusedRounds; r++) {
                 const int b = g16 + 64 * r;
                 if (b < nblk) {
-                    const uint4 q16 = (amax > 0.0f) ? quant16_auto(xr[m][r], sxm, rsm) : make_uint4(0, 0, 0, 0);
-                    if (blockIdx.x == 0)
-                        reinterpret_cast<uint4 *>(a.x_q_out + m * K)[(b * kRot + 16 * h16) / 16] = q16;
-                    // this lane's 16 values are logical words 8h .. 8h+7 of the block: lane
-                    // slot h >> 1, chunks 2 (h & 1) and 2 (h & 1) + 1
+                    float qv[16];
+                    quant16_values(xr[m][r], sxm, rsm, amax > 0.0f, qv);
+                    if (blockIdx.x == 0) {
+                        uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+                        for (int i = 0; i < 16; i++) wd[i >> 2] |= ((uint32_t)(int32_t)qv[i] & 0xFFu) << (8 * (i & 3));
+                        reinterpret_cast<uint4 *>(a.x_q_out + m * K)[(b * kRot + 16 * h16) / 16] =
+                            make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    }
+                    // fp16 pairs straight from the integers (exact: |q| <= 127); this lane's
+                    // 16 values are logical words 8h .. 8h+7 of the block: lane slot h >> 1,
+                    // chunks 2 (h & 1) and 2 (h & 1) + 1
+                    uint32_t hp[8];
+#pragma unroll
+                    for (int i = 0; i < 8; i++)
+                        hp[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(qv[2 * i], qv[2 * i + 1]));
                     const int lj = h16 >> 1, c0 = 2 * (h16 & 1), sw = xchunk_swizzle(lj, b);
                     const int base = m * xtok + b * kXBlk + (lj << 4);
-                    *reinterpret_cast<uint4 *>(xs + base + ((c0 ^ sw) << 2)) =
-                        make_uint4(cvt2(q16.x, 0), cvt2(q16.x, 16), cvt2(q16.y, 0), cvt2(q16.y, 16));
-                    *reinterpret_cast<uint4 *>(xs + base + (((c0 + 1) ^ sw) << 2)) =
-                        make_uint4(cvt2(q16.z, 0), cvt2(q16.z, 16), cvt2(q16.w, 0), cvt2(q16.w, 16));
+                    *reinterpret_cast<uint4 *>(xs + base + ((c0 ^ sw) << 2)) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+                    *reinterpret_cast<uint4 *>(xs + base + (((c0 + 1) ^ sw) << 2)) = make_uint4(hp[4], hp[5], hp[6], hp[7]);
                 }
             }
         }
