@@ -76,21 +76,46 @@ __device__ __forceinline__ void fwht256_lane4(float v[4], int lane) {
 // spans 1..8 are in-lane; element bits 4..7 (the "high nibble" h) are spread over the row's
 // lanes as h = t ^ 3*bit2(t) for row position t.  Under that map, flipping element bit 4, 5,
 // 6 or 7 is lane xor 1, 2, 7 or 8: the DPP patterns quad_perm [1,0,3,2], quad_perm [2,3,0,1],
-// row_half_mirror and row_ror:8, each a single exchange within the row.  A cross-lane
-// butterfly computes fma(+-1, own, partner): exactly one rounding of (lower + upper) on the
-// lower lane and (lower - upper) on the upper lane, so the result is bit-identical to the
-// add/subtract order above.  Every lane of the row must execute it.
+// row_half_mirror and row_ror:8, each a single exchange within the row.
+// A cross-lane butterfly is one fma with the partner's value as the DPP operand,
+// fma(partner, +-1, own): the lower lane gets RN(upper + lower) and the upper lane
+// RN(upper - lower), the negation of the subtraction's rounded result.  Each value is thus
+// held with the sign (-1)^(number of stages in which its lane was the upper one), that is
+// (-1)^popcount(h) at the end, which the final exact scaling by +-1/16 removes: the result
+// is bit-identical to the add/subtract order above (a zero may come out as -0).  Every lane
+// of the row must execute it.
 __device__ __forceinline__ int fwht_row16_nibble(int t) { return t ^ (((t >> 2) & 1) * 3); }
 
-template <int CTRL>
-__device__ __forceinline__ void fwht_row16_stage(float v[16], float sgn) {
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-        const float p = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(v[q]), CTRL, 0xF, 0xF, false));
-        v[q] = fmaf(sgn, v[q], p);
-    }
-}
+// One cross-lane stage: sixteen v_fmac_f32 with the DPP pattern on the multiplicand.  The
+// s_nop covers the two wait states a DPP read needs after the VALU write of its source.
+#define W4A8_FMAC_DPP16(PAT)                                                                        \
+    asm volatile("s_nop 1\n"                                                                      \
+                 "v_fmac_f32_dpp %0, %0, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %1, %1, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %2, %2, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %3, %3, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %4, %4, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %5, %5, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %6, %6, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %7, %7, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %8, %8, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %9, %9, %16 " PAT " row_mask:0xf bank_mask:0xf\n"                 \
+                 "v_fmac_f32_dpp %10, %10, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 "v_fmac_f32_dpp %11, %11, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 "v_fmac_f32_dpp %12, %12, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 "v_fmac_f32_dpp %13, %13, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 "v_fmac_f32_dpp %14, %14, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 "v_fmac_f32_dpp %15, %15, %16 " PAT " row_mask:0xf bank_mask:0xf\n"               \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),        \
+                   "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),      \
+                   "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])                              \
+                 : "v"(sgn))
+
+__device__ __forceinline__ void fwht_row16_stage_xor1(float v[16], float sgn) { W4A8_FMAC_DPP16("quad_perm:[1,0,3,2]"); }
+__device__ __forceinline__ void fwht_row16_stage_xor2(float v[16], float sgn) { W4A8_FMAC_DPP16("quad_perm:[2,3,0,1]"); }
+__device__ __forceinline__ void fwht_row16_stage_mirror(float v[16], float sgn) { W4A8_FMAC_DPP16("row_half_mirror"); }
+__device__ __forceinline__ void fwht_row16_stage_ror8(float v[16], float sgn) { W4A8_FMAC_DPP16("row_ror:8"); }
+#undef W4A8_FMAC_DPP16
 
 __device__ __forceinline__ void fwht256_row16(float v[16], int t) {
 #pragma unroll
@@ -104,12 +129,13 @@ __device__ __forceinline__ void fwht256_row16(float v[16], int t) {
         }
     }
     const int h = fwht_row16_nibble(t);
-    fwht_row16_stage<0xB1>(v, (h & 1) ? -1.0f : 1.0f);   // span 16:  lane ^ 1
-    fwht_row16_stage<0x4E>(v, (h & 2) ? -1.0f : 1.0f);   // span 32:  lane ^ 2
-    fwht_row16_stage<0x141>(v, (h & 4) ? -1.0f : 1.0f);  // span 64:  lane ^ 7 (half mirror)
-    fwht_row16_stage<0x128>(v, (h & 8) ? -1.0f : 1.0f);  // span 128: lane ^ 8 (rotate by 8)
+    fwht_row16_stage_xor1(v, (h & 1) ? -1.0f : 1.0f);    // span 16:  lane ^ 1
+    fwht_row16_stage_xor2(v, (h & 2) ? -1.0f : 1.0f);    // span 32:  lane ^ 2
+    fwht_row16_stage_mirror(v, (h & 4) ? -1.0f : 1.0f);  // span 64:  lane ^ 7 (half mirror)
+    fwht_row16_stage_ror8(v, (h & 8) ? -1.0f : 1.0f);    // span 128: lane ^ 8 (rotate by 8)
+    const float scale = (__builtin_popcount(h) & 1) ? -0.0625f : 0.0625f;
 #pragma unroll
-    for (int q = 0; q < 16; q++) v[q] = v[q] * 0.0625f;
+    for (int q = 0; q < 16; q++) v[q] = v[q] * scale;
 }
 
 // Sixteen consecutive activations (fp32, or bf16 widened exactly) starting at element off
