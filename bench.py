@@ -1,22 +1,25 @@
 """Benchmark of the W4A8 codebook linear layer on one MI355X.
 
 Headline (one JSON line on stdout): effective weight GB/s of the decode hot path at M=1.
-One step = the whole per-call path for one token on the two MLP shapes of a 27B-class
-decoder -- Hadamard-256 rotation + per-token int8 quantisation + W4A8 product, for gate/up
-(N=17408, K=5120) and for down (N=5120, K=17408), one fused launch each (w4a8_forward) --
-with inputs resident in HBM.  Each shape has 8 distinct weight copies (~400 MB per shape,
-beyond the 256 MB Infinity Cache) and consecutive steps use consecutive copies, so every
-step streams its weights from HBM.  Steps are replayed from HIP graphs (8 steps per graph)
-so host launch cost does not pace the GPU.
+One step = the MLP block of a 27B-class decoder for one token: Hadamard-256 rotation +
+per-token int8 quantisation + W4A8 product for gate and up (N=17408, K=5120, one input, one
+fused launch: w4a8_forward_multi) and for down (N=5120, K=17408, its own input: w4a8_forward),
+with inputs resident in HBM.  There are 8 distinct copies of the block's weights (~1.2 GB,
+beyond the 256 MB Infinity Cache) and consecutive steps use consecutive copies, so every step
+streams its weights from HBM.  Steps are replayed from HIP graphs (8 steps per graph) so host
+launch cost does not pace the GPU.  The nonlinearity between up and down is not part of the
+layer; down reads a synthetic input of its own.
 
-value = weight-side bytes per step (packed + group scales + row scales + codebook of both
+value = weight-side bytes per step (packed + group scales + row scales + codebook of the three
 matrices) / measured time per step.  The same line carries:
-  roofline      the fused decode kernel k_gemv<1,XIN=1>: algorithmic bytes per launch / its
-                average launch duration (HIP events on the launch stream around the timed
-                region) against 8 TB/s; traffic = HBM bytes per launch from rocprofv3
-                FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration, when the
-                committed counter summary matches the current kernel source (else null);
-  gemv          the same for the prepared-input GEMV kernel (w4a8_linear, M=1);
+  roofline      the dominant kernel, the fused gate+up launch k_gemv<1,1,8>: algorithmic
+                bytes per launch / its average launch duration (HIP events on the launch
+                stream around graph replays of that launch) against 8 TB/s; traffic = HBM
+                bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
+                copy-kernel calibration, when the committed counter summary matches the
+                current kernel source (else null);
+  down          the same figures for the fused down launch k_gemv<1,1,1>;
+  gemv          the prepared-input GEMV kernel (w4a8_linear, M=1, one layer) on both shapes;
   sweep         batched decode: M in {1,2,4,8,16,32,64} x four projection shapes, every
                 kernel that supports the point, plus the automatic choice (prepare included);
   model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
@@ -177,22 +180,50 @@ def cpu_baseline(shapes, target_s=10.0):
                        f"shapes 17408x5120 and 5120x17408, {el:.1f} s")
 
 
+def mlp_layers(w, torch, S, copies):
+    """`copies` distinct MLP blocks of the 27B-class shape: gate and up 17408x5120, down
+    5120x17408 (each block's weights are its own allocations, so nothing stays cached)."""
+    gu, dn = S.MLP_GATE_UP, S.MLP_DOWN
+    L = build_layers(w, torch, [gu, dn], 2 * copies)
+    return [dict(gate=L[gu][2 * c], up=L[gu][2 * c + 1], down=L[dn][c]) for c in range(copies)]
+
+
+def multi_forward_bytes(n, k, g, m=1):
+    """Algorithmic HBM bytes of one fused multi-layer forward launch over g layers of n x k:
+    the weights, fp32 x in once, x_q and s_x out once, fp32 y of every layer."""
+    return g * weight_bytes(n, k) + 4 * m * k + m * k + 4 * m + 4 * m * n * g
+
+
 def decode(w, torch, S, args, shapes):
-    """The headline: fused decode step over both MLP shapes, plus the per-kernel rooflines."""
-    layers = build_layers(w, torch, shapes, COPIES)
-    xs = {(n, k): torch.from_numpy(S.activations(1, k, seed=0)).cuda() for (n, k) in shapes}
-    xqs = {(n, k): (torch.empty((1, k), dtype=torch.int8, device="cuda"),
-                    torch.empty((1,), dtype=torch.float32, device="cuda")) for (n, k) in shapes}
-    ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
+    """The headline: one decode step of the MLP block at M=1 -- gate and up in one fused launch
+    (w4a8_forward_multi: rotate + quantise the MLP input, then both products), down in a second
+    (w4a8_forward on its own input) -- plus the per-kernel rooflines."""
+    (ng, kg), (nd, kd) = S.MLP_GATE_UP, S.MLP_DOWN
+    blocks = mlp_layers(w, torch, S, COPIES)
+    x_in = torch.from_numpy(S.activations(1, kg, seed=0)).cuda()
+    x_hid = torch.from_numpy(S.activations(1, kd, seed=1)).cuda()
+    xq_in = (torch.empty((1, kg), dtype=torch.int8, device="cuda"), torch.empty((1,), dtype=torch.float32, device="cuda"))
+    xq_hid = (torch.empty((1, kd), dtype=torch.int8, device="cuda"), torch.empty((1,), dtype=torch.float32, device="cuda"))
+    y_gu = [torch.empty((1, ng), dtype=torch.float32, device="cuda") for _ in range(2)]
+    y_dn = torch.empty((1, nd), dtype=torch.float32, device="cuda")
+
+    def gate_up(c):
+        b = blocks[c]
+        w.forward_multi(x_in, [b["gate"], b["up"]], outs=y_gu, x_q=xq_in[0], s_x=xq_in[1])
+
+    def down(c):
+        w.forward(x_hid, blocks[c]["down"], out=y_dn, x_q=xq_hid[0], s_x=xq_hid[1])
 
     def step(c):
-        for sh in shapes:
-            w.forward(xs[sh], layers[sh][c], out=ys[sh], x_q=xqs[sh][0], s_x=xqs[sh][1])
+        gate_up(c)
+        down(c)
 
     def step_unfused(c):
-        for sh in shapes:
-            w.prepare_activation(xs[sh], out=xqs[sh])
-            w.linear(*xqs[sh], layers[sh][c], out=ys[sh])
+        b = blocks[c]
+        w.prepare_activation(x_in, out=xq_in)
+        w.linear_multi(*xq_in, [b["gate"], b["up"]], outs=y_gu)
+        w.prepare_activation(x_hid, out=xq_hid)
+        w.linear(*xq_hid, b["down"], out=y_dn)
 
     full = make_graph(torch, lambda: [step(c) for c in range(COPIES)])
     rem = args.steps % COPIES
@@ -217,42 +248,52 @@ def decode(w, torch, S, args, shapes):
     wall = time.perf_counter() - t0
     el = ev0.elapsed_time(ev1) * 1e-3
     ms_step = el * 1e3 / args.steps
-    wb = sum(weight_bytes(n, k) for (n, k) in shapes)
+    wb = 2 * weight_bytes(ng, kg) + weight_bytes(nd, kd)
     value = wb / (el / args.steps) / 1e9
-    log(f"decode step: {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth "
+    log(f"decode step (MLP block): {ms_step * 1e3:.2f} us, {value:.1f} GB/s effective weight bandwidth "
         f"(host wall clock incl. the busy-wait kernel {wall:.3f} s)")
 
-    # the dominant kernel is the fused forward: 2 launches per step, back to back
-    t_fwd = el / (2 * args.steps)
-    per_fwd = sum(forward_bytes(n, k) for (n, k) in shapes) / len(shapes)
-    ach = per_fwd / t_fwd / 1e9
+    # the dominant kernel: the fused gate+up launch (two thirds of the step's bytes), timed in a
+    # graph of its own launches; the down launch beside it
+    reps = max(4, args.steps // (4 * COPIES))
+    g_gu = make_graph(torch, lambda: [gate_up(c) for c in range(COPIES)])
+    t_gu = time_graph(torch, g_gu, reps) / COPIES
+    g_dn = make_graph(torch, lambda: [down(c) for c in range(COPIES)])
+    t_dn = time_graph(torch, g_dn, reps) / COPIES
+    per_gu = multi_forward_bytes(ng, kg, 2)
+    per_dn = forward_bytes(nd, kd)
+    ach = per_gu / t_gu / 1e9
     traffic = measured_traffic()
     roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="k_gemv<1,1> (fused rotate + quantise + W4A8 GEMV, fp32 x)",
-                    per_launch_bytes=int(per_fwd), avg_launch_us=round(t_fwd * 1e6, 3))
-    log(f"fused forward: {t_fwd * 1e6:.2f} us per launch, {ach:.1f} GB/s algorithmic, "
-        f"traffic {traffic}")
+                    kernel="k_gemv<1,1,8> (fused rotate + quantise + W4A8 GEMV of gate and up, fp32 x)",
+                    per_launch_bytes=int(per_gu), avg_launch_us=round(t_gu * 1e6, 3))
+    down_k = dict(kernel="k_gemv<1,1,1> (fused rotate + quantise + W4A8 GEMV of down, fp32 x)",
+                  avg_launch_us=round(t_dn * 1e6, 3), per_launch_bytes=int(per_dn),
+                  achieved=round(per_dn / t_dn / 1e9, 1), frac=round(per_dn / t_dn / 1e9 / HBM_PEAK_GBS, 4))
+    log(f"fused gate+up: {t_gu * 1e6:.2f} us per launch, {ach:.1f} GB/s algorithmic, traffic {traffic}; "
+        f"fused down: {t_dn * 1e6:.2f} us, {per_dn / t_dn / 1e9:.1f} GB/s")
 
-    reps = max(4, args.steps // (4 * COPIES))
     unf = make_graph(torch, lambda: [step_unfused(c) for c in range(COPIES)])
     t_unf = time_graph(torch, unf, reps) / COPIES
     log(f"decode step with separate prepare launches: {t_unf * 1e6:.2f} us")
 
-    for sh in shapes:
-        w.prepare_activation(xs[sh], out=xqs[sh])
+    # the single-layer GEMV on prepared activations, both MLP shapes
+    w.prepare_activation(x_in, out=xq_in)
+    w.prepare_activation(x_hid, out=xq_hid)
     torch.cuda.synchronize()
-    gemv_g = make_graph(torch, lambda: [w.linear(*xqs[sh], layers[sh][c], out=ys[sh], algo=w.ALGO_GEMV)
-                                        for c in range(COPIES) for sh in shapes])
-    t_gemv = time_graph(torch, gemv_g, reps) / (COPIES * len(shapes))
-    per_gemv = sum(gemv_bytes(n, k) for (n, k) in shapes) / len(shapes)
+    gemv_g = make_graph(torch, lambda: [(w.linear(*xq_in, blocks[c]["gate"], out=y_gu[0], algo=w.ALGO_GEMV),
+                                         w.linear(*xq_hid, blocks[c]["down"], out=y_dn, algo=w.ALGO_GEMV))
+                                        for c in range(COPIES)])
+    t_gemv = time_graph(torch, gemv_g, reps) / (COPIES * 2)
+    per_gemv = (gemv_bytes(ng, kg) + gemv_bytes(nd, kd)) / 2
     log(f"GEMV (prepared x_q): {t_gemv * 1e6:.2f} us per launch, {per_gemv / t_gemv / 1e9:.1f} GB/s")
-    gemv = dict(kernel="k_gemv<1,0> (prepared int8 x)", avg_launch_us=round(t_gemv * 1e6, 3),
+    gemv = dict(kernel="k_gemv<1,0,1> (prepared int8 x, one layer)", avg_launch_us=round(t_gemv * 1e6, 3),
                 per_launch_bytes=int(per_gemv), achieved=round(per_gemv / t_gemv / 1e9, 1),
                 frac=round(per_gemv / t_gemv / 1e9 / HBM_PEAK_GBS, 4))
-    out = dict(value=value, ms_step=ms_step, warm=warm, wb=wb, roofline=roofline, gemv=gemv,
+    out = dict(value=value, ms_step=ms_step, warm=warm, wb=wb, roofline=roofline, gemv=gemv, down=down_k,
                unfused_step_us=round(t_unf * 1e6, 2), tokens_per_s=round(1.0 / (el / args.steps), 1))
-    del layers
+    del blocks
     return out
 
 
@@ -511,29 +552,35 @@ def w8a8_model(w, torch, S, tokens=10):
 
 def pmc_pass(w, torch, S, shapes):
     """Eager launches for the counter runs: a plain elementwise copy of CALIB_BYTES (reads and
-    writes that many bytes once) for calibration, then the fused forward and the prepared-input
-    GEMV on every weight copy, then the two prefill GEMMs."""
+    writes that many bytes once) for calibration, then the MLP block's fused launches (gate+up,
+    down) and the prepared-input GEMV on every weight copy, then the two prefill GEMMs."""
     a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
         torch.neg(a, out=b)
     torch.cuda.synchronize()
     del a, b
-    layers = build_layers(w, torch, shapes, COPIES)
-    for sh in shapes:
-        x = torch.from_numpy(S.activations(1, sh[1], seed=0)).cuda()
-        xq, sx = w.prepare_activation(x)
-        y = torch.empty((1, sh[0]), dtype=torch.float32, device="cuda")
-        for c in range(COPIES):
-            w.forward(x, layers[sh][c], out=y, x_q=xq, s_x=sx)
-        for c in range(COPIES):
-            w.linear(xq, sx, layers[sh][c], out=y, algo=w.ALGO_GEMV)
+    (ng, kg), (nd, kd) = S.MLP_GATE_UP, S.MLP_DOWN
+    blocks = mlp_layers(w, torch, S, COPIES)
+    x_in = torch.from_numpy(S.activations(1, kg, seed=0)).cuda()
+    x_hid = torch.from_numpy(S.activations(1, kd, seed=1)).cuda()
+    xq_in, sx_in = w.prepare_activation(x_in)
+    xq_hid, sx_hid = w.prepare_activation(x_hid)
+    y_gu = [torch.empty((1, ng), dtype=torch.float32, device="cuda") for _ in range(2)]
+    y_dn = torch.empty((1, nd), dtype=torch.float32, device="cuda")
+    for c in range(COPIES):
+        w.forward_multi(x_in, [blocks[c]["gate"], blocks[c]["up"]], outs=y_gu, x_q=xq_in, s_x=sx_in)
+    for c in range(COPIES):
+        w.forward(x_hid, blocks[c]["down"], out=y_dn, x_q=xq_hid, s_x=sx_hid)
+    for c in range(COPIES):
+        w.linear(xq_in, sx_in, blocks[c]["gate"], out=y_gu[0], algo=w.ALGO_GEMV)
+        w.linear(xq_hid, sx_hid, blocks[c]["down"], out=y_dn, algo=w.ALGO_GEMV)
     torch.cuda.synchronize()
-    for (n, k) in shapes:
+    for (n, k), L in ((S.MLP_GATE_UP, blocks[0]["gate"]), (S.MLP_DOWN, blocks[0]["down"])):
         xq, sx = w.prepare_activation(torch.from_numpy(S.activations(2048, k, seed=0)).cuda())
         y = torch.empty((2048, n), dtype=torch.float32, device="cuda")
         for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16):
-            w.linear(xq, sx, layers[(n, k)][0], out=y, algo=algo)
+            w.linear(xq, sx, L, out=y, algo=algo)
     torch.cuda.synchronize()
     log("pmc pass done")
 
@@ -574,14 +621,16 @@ def main():
         "steps": args.steps, "warmup": d["warm"], "ms_per_step": round(d["ms_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "decode M=1: rotate + int8-quantise + W4A8 product (w4a8_forward), "
-                               "gate/up 17408x5120 and down 5120x17408, "
-                               f"{COPIES} distinct weight copies per shape",
+        "config": {"workload": "decode M=1 of a 27B-class MLP block: rotate + int8-quantise + W4A8 "
+                               "product, gate and up 17408x5120 in one fused launch "
+                               "(w4a8_forward_multi), down 5120x17408 in a second (w4a8_forward); "
+                               f"{COPIES} distinct weight copies of the block",
                    "tokens": 1, "weight_bytes_per_step": d["wb"]},
         "tokens_per_s": d["tokens_per_s"],
         "unfused_step_us": d["unfused_step_us"],
         "roofline": d["roofline"],
         "gemv": d["gemv"],
+        "down": d["down"],
     }
     if not args.no_sweep:
         out["sweep"] = sweep(w, torch, S)

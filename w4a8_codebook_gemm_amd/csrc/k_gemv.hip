@@ -49,6 +49,7 @@ constexpr int kTabWords = 256 * 64;                 // 64 KiB
 constexpr int kLdsMax = 160 * 1024;                 // gfx950 LDS per workgroup
 constexpr int kMaxMT = 4;
 constexpr int kMaxXChunks = 40960 / 8 / kThreads;  // 8-value activation chunks per thread
+constexpr int kScaleLoads = 4;                     // 16-byte group-scale loads per thread: <= 64 KiB per workgroup
 // Activation words per 256-wide K block in LDS (128 fp16 pairs, unpadded).  Lane j of a
 // group reads the 16 words 16j .. 16j+15 of its block as four 4-word chunks, chunk c stored
 // at position c ^ ((j >> 1) & 3) ^ (block & 1): the 8 lanes of one group cover 32 of the 64
@@ -62,7 +63,12 @@ __device__ __forceinline__ int xchunk_swizzle(int j, int block) { return ((j >> 
 constexpr int kFusedRounds = 2;
 
 template <int MT>
-constexpr int depth() { return 2; }  // units in flight per 8-lane group (more only adds contention)
+constexpr int depth() { return 2; }
+
+// LDS bytes of the staged group scales: whole 1 KiB blocks (one wave's copy)
+__host__ __device__ __forceinline__ int64_t scale_lds_bytes(int64_t rows, int64_t grpbytes) {
+    return (rows * grpbytes + 1023) & ~(int64_t)1023;
+}  // units in flight per 8-lane group (more only adds contention)
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
@@ -203,12 +209,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     const int units = P * nblk;
     const int pstride = nblk | 1;                                // odd: conflict-free row sums
     const int xtok = nblk * kXBlk;                               // LDS words per token
+    const uint32_t grpbytes = (uint32_t)(K / kGroup);
     uint32_t *xs = dyn;                                          // [MT][nblk][kXBlk] fp16 pairs
-    float *part = reinterpret_cast<float *>(xs + MT * xtok);     // [MT][rows_per_wg][pstride]
+    uint8_t *ss = reinterpret_cast<uint8_t *>(xs + MT * xtok);   // [rows_per_wg][K/16] e4m3 scales
+    float *part = reinterpret_cast<float *>(ss + scale_lds_bytes(rows_per_wg, grpbytes));  // [MT][rows_per_wg][pstride]
 
     const int j = tid & 7;
     const uint32_t lanebase = (uint32_t)(tid & 63) * 4u;
-    const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
+    const uint32_t rowbytes = (uint32_t)(K / 2);
     // Workgroup-relative 32-bit offsets into buffer resources bounded by this workgroup's
     // rows: row 2rp+1 past the last row reads as zero and is never stored.
     const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
@@ -254,12 +262,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // in-order load counter exact); a unit past the end gets an offset beyond the buffer,
     // which reads as zero without touching memory.
     constexpr uint32_t kOutside = 0x80000000u;
-    auto fetch = [&](const Slot &sl, u32x4 &pa, u32x4 &pb, uint32_t &sa, uint32_t &sb) {
-        const uint32_t op = sl.valid ? sl.op : kOutside, os = sl.valid ? sl.os : kOutside;
+    auto fetch = [&](const Slot &sl, u32x4 &pa, u32x4 &pb) {
+        const uint32_t op = sl.valid ? sl.op : kOutside;
         pa = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op, 0, kNT);
         pb = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op + rowbytes, 0, kNT);
-        sa = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os, 0, kNT);
-        sb = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os + grpbytes, 0, kNT);
     };
 
     // Small operands first: the row scales of this workgroup's rows (one per thread, kept
@@ -310,6 +316,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
             }
     }
 
+    // The workgroup's group scales (nrow x K/16 contiguous bytes) are copied to LDS by the
+    // buffer unit (16 bytes per lane straight into LDS, no registers), so the weight stream
+    // carries no 2-byte loads.  A wave copies a 1 KiB block when its first byte is inside the
+    // region; the allocation is rounded up to whole blocks.
+    const int nsc = (int)(nrow * grpbytes / 16);
+#pragma unroll
+    for (int q = 0; q < kScaleLoads; q++) {
+        const int blk = q * kThreads + 64 * wave;  // first 16-byte chunk of this wave's block
+        if (blk < nsc)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs_s, (__attribute__((address_space(3))) void *)(ss + 16 * blk), 16,
+                16u * (uint32_t)(blk + (tid & 63)), 0, 0, kNT);
+    }
+
     // A ring of kDepth units in flight per lane group; the first loads are issued before
     // the prologue so their HBM latency overlaps the table build.  The scheduling barrier
     // keeps every small operand's load ahead of them.
@@ -317,11 +337,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     constexpr int kDepth = depth<MT>();
     Slot cur[kDepth];
     u32x4 pa[kDepth], pb[kDepth];
-    uint32_t sa[kDepth], sb[kDepth];
 #pragma unroll
     for (int d = 0; d < kDepth; d++) {
         cur[d] = make_slot();
-        fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
+        fetch(cur[d], pa[d], pb[d]);
         step();
     }
 
@@ -419,10 +438,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
             }
         }
     }
+    // every copy to LDS of this wave is complete once at most the ring's 2 x kDepth weight
+    // loads (issued after them) are outstanding: vmcnt(2 kDepth) (gfx9 encoding, no
+    // expcnt / lgkmcnt wait); the barrier then publishes them to the other waves
+    static_assert(2 * depth<MT>() < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * depth<MT>()));
     __syncthreads();
 
 
-    auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb, uint32_t sa, uint32_t sb) {
+    auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb) {
+        // the two rows' scale pairs of this lane's 32 values (row 2rp + 1 past the last row
+        // reads stale LDS; its partial is never used)
+        const uint32_t sa = *reinterpret_cast<const uint16_t *>(ss + sl.os);
+        const uint32_t sb = *reinterpret_cast<const uint16_t *>(ss + sl.os + grpbytes);
         const int xbase = sl.xw;
         const int xsw = xchunk_swizzle(j, xbase >> 7);
         uint32_t xv[MT][16];
@@ -455,9 +483,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     while (__builtin_amdgcn_readfirstlane(bu) - kDepth * kLaneGroups < units) {
 #pragma unroll
         for (int d = 0; d < kDepth; d++) {
-            if (cur[d].valid) compute(cur[d], pa[d], pb[d], sa[d], sb[d]);
+            if (cur[d].valid) compute(cur[d], pa[d], pb[d]);
             cur[d] = make_slot();
-            fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
+            fetch(cur[d], pa[d], pb[d]);
             step();
         }
     }
@@ -497,6 +525,13 @@ hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int nu
     const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4 + (XIN ? (int64_t)MT * (kThreads / 64) * 4 : 0);
     const int64_t dyn_max = kLdsMax - (int64_t)kTabWords * 4;
     const int64_t pstride = nblk | 1;
+    const int64_t grpbytes = a.K / kGroup;
+    // LDS bytes for a workgroup of `rows` rows: partials plus staged group scales (at most
+    // kScaleLoads 16-byte copies per thread in all)
+    auto need = [&](int64_t rows) { return fixed + scale_lds_bytes(rows, grpbytes) + (int64_t)MT * rows * pstride * 4; };
+    auto fits = [&](int64_t rows) {
+        return need(rows) <= dyn_max && rows * grpbytes <= (int64_t)kScaleLoads * kThreads * 16;
+    };
     int64_t total = 0;
     for (int g = 0; g < G; g++) total += layers[g].N;
     // one workgroup per CU in all, shared out in proportion to the layers' rows; a layer's
@@ -510,8 +545,8 @@ hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int nu
         if (want < 1) want = 1;
         int64_t rows = (n + want - 1) / want;
         rows += rows & 1;
-        while (rows > 2 && fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) rows = ((rows / 2) + 1) & ~1LL;
-        if (fixed + (int64_t)MT * rows * pstride * 4 > dyn_max) return hipErrorInvalidValue;
+        while (rows > 2 && !fits(rows)) rows = ((rows / 2) + 1) & ~1LL;
+        if (!fits(rows)) return hipErrorInvalidValue;
         gt.wg_start[g] = (int)wg;
         gt.rows[g] = (int)rows;
         gt.L[g] = layers[g];
@@ -519,7 +554,7 @@ hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int nu
         if (rows > max_rows) max_rows = rows;
     }
     gt.wg_start[G] = (int)wg;
-    const int64_t lds = fixed + (int64_t)MT * max_rows * pstride * 4;
+    const int64_t lds = need(max_rows);
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN, NG>),
