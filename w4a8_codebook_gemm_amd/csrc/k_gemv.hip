@@ -20,13 +20,15 @@
 //    bits 2..7 in one v_perm, the read is conflict-free, and one v_dot2_f32_f16 with the
 //    fp16 pair of activations (int8 values, exact in fp16) gives two products with fp32
 //    accumulation.  Relative error of the fp16 codebook is at most 2^-11 per level.
-//  * Latency: each 8-lane group keeps two units (512 B) in flight in a register ring
-//    (a unit's slot is refilled with the loads of the unit kDepth ahead as soon as it is
-//    consumed); the first loads go out before the table build; the weight stream uses
-//    non-temporal buffer loads with workgroup-relative 32-bit offsets.
-//  * Units run in row-major order, so a wave reads 1 KiB contiguous per row and its group
-//    scales as one 128-B run; the activation chunks in LDS are XOR-swizzled by lane and by
-//    block parity so that the two groups served together cover all 64 LDS banks.
+//  * Latency: each 8-lane group issues two units (512 B) before the prologue, so their
+//    HBM latency overlaps the table build; from then on one unit is in flight while one is
+//    computed (its loads go out before the compute).  More bytes in flight than that only
+//    adds contention in HBM.  The weight stream uses non-temporal buffer loads with
+//    workgroup-relative 32-bit offsets.
+//  * Units run in row-major order, so a wave reads 1 KiB contiguous per row; the group
+//    scales of the workgroup's rows are copied to LDS up front by the buffer unit (16 B per
+//    lane); the activation chunks in LDS are XOR-swizzled by lane and by block parity so
+//    that the two groups served together cover all 64 LDS banks.
 //  * Each group's two-element dot products are summed in fp32, scaled by the decoded e4m3
 //    group scale, reduced over the 8 lanes with xor shuffles, and written to an LDS
 //    partial per (row, block) (odd row stride: conflict-free); eight lanes per row then
@@ -332,8 +334,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
 
     // A ring of kDepth units in flight per lane group; the first loads are issued before
     // the prologue so their HBM latency overlaps the table build.  The scheduling barrier
-    // keeps every small operand's load ahead of them.
+    // keeps every small operand's load ahead of them; with raw activations (a larger first
+    // request per wave) the workgroup barrier also keeps every wave's small loads ahead of
+    // any wave's weight stream.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XIN != 0) __syncthreads();
     constexpr int kDepth = depth<MT>();
     Slot cur[kDepth];
     u32x4 pa[kDepth], pb[kDepth];
@@ -480,14 +485,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
         }
     };
 
-    while (__builtin_amdgcn_readfirstlane(bu) - kDepth * kLaneGroups < units) {
-#pragma unroll
-        for (int d = 0; d < kDepth; d++) {
-            if (cur[d].valid) compute(cur[d], pa[d], pb[d]);
-            cur[d] = make_slot();
-            fetch(cur[d], pa[d], pb[d]);
-            step();
-        }
+    // Two units went out before the prologue (they cover its latency).  From then on one unit
+    // is in flight while a unit is computed: the next unit's loads are issued first, into the
+    // slot computed last.  bu is the base of the next fetch, so slot 1 holds base bu - 128.
+    static_assert(depth<MT>() == 2, "two slots");
+    if (cur[0].valid) compute(cur[0], pa[0], pb[0]);
+    while (__builtin_amdgcn_readfirstlane(bu) - kLaneGroups < units) {
+        cur[0] = make_slot();
+        fetch(cur[0], pa[0], pb[0]);
+        step();
+        if (cur[1].valid) compute(cur[1], pa[1], pb[1]);
+        cur[1] = make_slot();
+        fetch(cur[1], pa[1], pb[1]);
+        step();
+        if (cur[0].valid) compute(cur[0], pa[0], pb[0]);
     }
     __syncthreads();
 
