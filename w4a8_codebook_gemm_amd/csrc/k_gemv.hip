@@ -81,33 +81,30 @@ __device__ __forceinline__ uint32_t tab_read(const uint32_t *lds, uint32_t byte_
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(lds) + byte_addr);
 }
 
-// Both rows of a unit (2 x 16 packed bytes) against MT token vectors.  All 32 table reads
-// are issued before the first dot product so one LDS round trip covers the whole unit;
-// each group's 8 products are split over two accumulators to shorten the dependency
-// chain.  g[row][group] receives the group partials.
-template <int MT>
-__device__ __forceinline__ void unit_dots(const uint32_t *lds, uint32_t lanebase, const u32x4 &pa,
-                                          const u32x4 &pb, const uint32_t (&xv)[MT][16],
-                                          float (&g)[MT][2][2]) {
+// The fp16 codebook pairs of both rows of a unit (2 x 16 packed bytes): all 32 table reads
+// are issued together so one LDS round trip covers the whole unit.
+__device__ __forceinline__ void unit_pairs(const uint32_t *lds, uint32_t lanebase, const u32x4 &pa,
+                                           const u32x4 &pb, uint32_t (&pair)[32]) {
     const uint32_t w[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    uint32_t pair[32];
 #pragma unroll
     for (int i = 0; i < 32; i++)
         pair[i] = tab_read(lds, __builtin_amdgcn_perm(lanebase, w[i >> 2], 0x0C0C0004u | ((i & 3) << 8)));
+}
+
+// One token's group partials g[row][group] of a unit; each group's 8 products are split over
+// two accumulators to shorten the dependency chain.
+__device__ __forceinline__ void unit_dots(const uint32_t (&pair)[32], const uint32_t (&xv)[16], float (&g)[2][2]) {
 #pragma unroll
-    for (int m = 0; m < MT; m++) {
+    for (int r = 0; r < 2; r++) {
 #pragma unroll
-        for (int r = 0; r < 2; r++) {
+        for (int gi = 0; gi < 2; gi++) {
+            float e0 = 0.0f, e1 = 0.0f;
 #pragma unroll
-            for (int gi = 0; gi < 2; gi++) {
-                float e0 = 0.0f, e1 = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 8; q += 2) {
-                    e0 = dot2(pair[16 * r + 8 * gi + q], xv[m][8 * gi + q], e0);
-                    e1 = dot2(pair[16 * r + 8 * gi + q + 1], xv[m][8 * gi + q + 1], e1);
-                }
-                g[m][r][gi] = e0 + e1;
+            for (int q = 0; q < 8; q += 2) {
+                e0 = dot2(pair[16 * r + 8 * gi + q], xv[8 * gi + q], e0);
+                e1 = dot2(pair[16 * r + 8 * gi + q + 1], xv[8 * gi + q + 1], e1);
             }
+            g[r][gi] = e0 + e1;
         }
     }
 }
@@ -178,8 +175,9 @@ struct GroupTab {
 // XIN selects the activation input: 0 = prepared int8 x_q and s_x; 1 = fp32 and 2 = bf16
 // raw activations, rotated and quantised in the prologue with the arithmetic of the
 // activation kernel (every workgroup does the same, bit for bit; workgroup 0 also stores
-// x_q and s_x).
-template <int MT, int XIN, int NG>
+// x_q and s_x).  SS: the group scales are staged in LDS (else each unit loads its own two
+// bytes per row; used where the staging would cost rows per workgroup).
+template <int MT, int XIN, int NG, bool SS>
 __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt) {
     // The pair table is a static LDS array at a compile-time address, so each lookup is one
     // v_perm for the address and one ds_read_b32; activations and partials follow it in
@@ -214,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     const uint32_t grpbytes = (uint32_t)(K / kGroup);
     uint32_t *xs = dyn;                                          // [MT][nblk][kXBlk] fp16 pairs
     uint8_t *ss = reinterpret_cast<uint8_t *>(xs + MT * xtok);   // [rows_per_wg][K/16] e4m3 scales
-    float *part = reinterpret_cast<float *>(ss + scale_lds_bytes(rows_per_wg, grpbytes));  // [MT][rows_per_wg][pstride]
+    float *part = reinterpret_cast<float *>(ss + (SS ? scale_lds_bytes(rows_per_wg, grpbytes) : 0));  // [MT][rows_per_wg][pstride]
 
     const int j = tid & 7;
     const uint32_t lanebase = (uint32_t)(tid & 63) * 4u;
@@ -264,10 +262,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // in-order load counter exact); a unit past the end gets an offset beyond the buffer,
     // which reads as zero without touching memory.
     constexpr uint32_t kOutside = 0x80000000u;
-    auto fetch = [&](const Slot &sl, u32x4 &pa, u32x4 &pb) {
+    auto fetch = [&](const Slot &sl, u32x4 &pa, u32x4 &pb, uint32_t &sa, uint32_t &sb) {
         const uint32_t op = sl.valid ? sl.op : kOutside;
         pa = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op, 0, kNT);
         pb = __builtin_amdgcn_raw_buffer_load_b128(rs_p, op + rowbytes, 0, kNT);
+        if constexpr (!SS) {
+            const uint32_t os = sl.valid ? sl.os : kOutside;
+            sa = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os, 0, kNT);
+            sb = __builtin_amdgcn_raw_buffer_load_b16(rs_s, os + grpbytes, 0, kNT);
+        }
     };
 
     // Small operands first: the row scales of this workgroup's rows (one per thread, kept
@@ -322,9 +325,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // buffer unit (16 bytes per lane straight into LDS, no registers), so the weight stream
     // carries no 2-byte loads.  A wave copies a 1 KiB block when its first byte is inside the
     // region; the allocation is rounded up to whole blocks.
-    const int nsc = (int)(nrow * grpbytes / 16);
+    const int nsc = SS ? (int)(nrow * grpbytes / 16) : 0;
 #pragma unroll
-    for (int q = 0; q < kScaleLoads; q++) {
+    for (int q = 0; q < (SS ? kScaleLoads : 0); q++) {
         const int blk = q * kThreads + 64 * wave;  // first 16-byte chunk of this wave's block
         if (blk < nsc)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -342,10 +345,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     constexpr int kDepth = depth<MT>();
     Slot cur[kDepth];
     u32x4 pa[kDepth], pb[kDepth];
+    uint32_t sa[kDepth] = {}, sb[kDepth] = {};  // per-unit scale bytes when they are not staged
 #pragma unroll
     for (int d = 0; d < kDepth; d++) {
         cur[d] = make_slot();
-        fetch(cur[d], pa[d], pb[d]);
+        fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
         step();
     }
 
@@ -447,29 +451,34 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // loads (issued after them) are outstanding: vmcnt(2 kDepth) (gfx9 encoding, no
     // expcnt / lgkmcnt wait); the barrier then publishes them to the other waves
     static_assert(2 * depth<MT>() < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * depth<MT>()));
+    if constexpr (SS) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * depth<MT>()));
     __syncthreads();
 
 
-    auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb) {
-        // the two rows' scale pairs of this lane's 32 values (row 2rp + 1 past the last row
-        // reads stale LDS; its partial is never used)
-        const uint32_t sa = *reinterpret_cast<const uint16_t *>(ss + sl.os);
-        const uint32_t sb = *reinterpret_cast<const uint16_t *>(ss + sl.os + grpbytes);
+    auto compute = [&](const Slot &sl, const u32x4 &pa, const u32x4 &pb, uint32_t sa, uint32_t sb) {
+        // the two rows' scale pairs of this lane's 32 values (staged: row 2rp + 1 past the
+        // last row reads stale LDS; its partial is never used)
+        if constexpr (SS) {
+            sa = *reinterpret_cast<const uint16_t *>(ss + sl.os);
+            sb = *reinterpret_cast<const uint16_t *>(ss + sl.os + grpbytes);
+        }
         const int xbase = sl.xw;
         const int xsw = xchunk_swizzle(j, xbase >> 7);
-        uint32_t xv[MT][16];
+        uint32_t pair[32];
+        unit_pairs(lds, lanebase, pa, pb, pair);
+        // one token's activations at a time (16 registers live, whatever MT)
+        float g[MT][2][2];
 #pragma unroll
         for (int m = 0; m < MT; m++) {
+            uint32_t xv[16];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(xs + m * xtok + xbase + 4 * (q ^ xsw));  // xbase / 128 = block
-                xv[m][4 * q + 0] = v.x; xv[m][4 * q + 1] = v.y;
-                xv[m][4 * q + 2] = v.z; xv[m][4 * q + 3] = v.w;
+                xv[4 * q + 0] = v.x; xv[4 * q + 1] = v.y;
+                xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
             }
+            unit_dots(pair, xv, g[m]);
         }
-        float g[MT][2][2];
-        unit_dots<MT>(lds, lanebase, pa, pb, xv, g);
         // gfx950's v_cvt_f32_fp8 decodes OCP E4M3FN (checked on all 254 finite codes)
         const float fa0 = __builtin_amdgcn_cvt_f32_fp8((int)sa, 0), fa1 = __builtin_amdgcn_cvt_f32_fp8((int)sa, 1);
         const float fb0 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0), fb1 = __builtin_amdgcn_cvt_f32_fp8((int)sb, 1);
@@ -489,16 +498,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // is in flight while a unit is computed: the next unit's loads are issued first, into the
     // slot computed last.  bu is the base of the next fetch, so slot 1 holds base bu - 128.
     static_assert(depth<MT>() == 2, "two slots");
-    if (cur[0].valid) compute(cur[0], pa[0], pb[0]);
+    if (cur[0].valid) compute(cur[0], pa[0], pb[0], sa[0], sb[0]);
     while (__builtin_amdgcn_readfirstlane(bu) - kLaneGroups < units) {
         cur[0] = make_slot();
-        fetch(cur[0], pa[0], pb[0]);
+        fetch(cur[0], pa[0], pb[0], sa[0], sb[0]);
         step();
-        if (cur[1].valid) compute(cur[1], pa[1], pb[1]);
+        if (cur[1].valid) compute(cur[1], pa[1], pb[1], sa[1], sb[1]);
         cur[1] = make_slot();
-        fetch(cur[1], pa[1], pb[1]);
+        fetch(cur[1], pa[1], pb[1], sa[1], sb[1]);
         step();
-        if (cur[0].valid) compute(cur[0], pa[0], pb[0]);
+        if (cur[0].valid) compute(cur[0], pa[0], pb[0], sa[0], sb[0]);
     }
     __syncthreads();
 
@@ -527,27 +536,28 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     }
 }
 
+// Rows per workgroup for each layer (one workgroup per CU in all, shared out in proportion
+// to the layers' rows; a layer's rows per workgroup are even and small enough for its LDS),
+// with or without the staged group scales.  Returns the dynamic LDS bytes, or -1.
 template <int MT, int XIN, int NG>
-hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
-    if (G < 1 || G > NG) return hipErrorInvalidValue;
+int64_t plan_rows(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, bool ss, GroupTab<NG> &gt) {
     const int64_t nblk = a.K / kRot;
-    // dynamic part (the 64 KiB table is static): activations, then a [MT][16] scratch for
-    // the fused preparation's wave maxima, then the partials
+    // dynamic part (the 64 KiB table is static): activations, staged scales, partials, then a
+    // [MT][16] scratch for the fused preparation's wave maxima
     const int64_t fixed = (int64_t)MT * nblk * kXBlk * 4 + (XIN ? (int64_t)MT * (kThreads / 64) * 4 : 0);
     const int64_t dyn_max = kLdsMax - (int64_t)kTabWords * 4;
     const int64_t pstride = nblk | 1;
     const int64_t grpbytes = a.K / kGroup;
-    // LDS bytes for a workgroup of `rows` rows: partials plus staged group scales (at most
-    // kScaleLoads 16-byte copies per thread in all)
-    auto need = [&](int64_t rows) { return fixed + scale_lds_bytes(rows, grpbytes) + (int64_t)MT * rows * pstride * 4; };
+    // staged scales: at most kScaleLoads 16-byte copies per thread in all
+    auto need = [&](int64_t rows) {
+        return fixed + (ss ? scale_lds_bytes(rows, grpbytes) : 0) + (int64_t)MT * rows * pstride * 4;
+    };
     auto fits = [&](int64_t rows) {
-        return need(rows) <= dyn_max && rows * grpbytes <= (int64_t)kScaleLoads * kThreads * 16;
+        return need(rows) <= dyn_max && (!ss || rows * grpbytes <= (int64_t)kScaleLoads * kThreads * 16);
     };
     int64_t total = 0;
     for (int g = 0; g < G; g++) total += layers[g].N;
-    // one workgroup per CU in all, shared out in proportion to the layers' rows; a layer's
-    // rows per workgroup are even and small enough for its partials to fit in LDS
-    GroupTab<NG> gt{};
+    gt = GroupTab<NG>{};
     gt.G = G;
     int64_t wg = 0, max_rows = 2;
     for (int g = 0; g < G; g++) {
@@ -557,7 +567,7 @@ hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int nu
         int64_t rows = (n + want - 1) / want;
         rows += rows & 1;
         while (rows > 2 && !fits(rows)) rows = ((rows / 2) + 1) & ~1LL;
-        if (!fits(rows)) return hipErrorInvalidValue;
+        if (!fits(rows)) return -1;
         gt.wg_start[g] = (int)wg;
         gt.rows[g] = (int)rows;
         gt.L[g] = layers[g];
@@ -565,17 +575,35 @@ hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int nu
         if (rows > max_rows) max_rows = rows;
     }
     gt.wg_start[G] = (int)wg;
-    const int64_t lds = need(max_rows);
+    return need(max_rows);
+}
+
+template <int MT, int XIN, int NG, bool SS>
+hipError_t launch_planned(const LinearArgs &a, const GroupTab<NG> &gt, int64_t lds, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN, NG>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN, NG, SS>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kLdsMax - kTabWords * 4));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((k_gemv<MT, XIN, NG>), dim3((unsigned)wg), dim3(kThreads), (size_t)lds, stream, a, gt);
+    hipLaunchKernelGGL((k_gemv<MT, XIN, NG, SS>), dim3((unsigned)gt.wg_start[gt.G]), dim3(kThreads), (size_t)lds, stream, a, gt);
     return hipGetLastError();
+}
+
+// The staged-scale kernel is used when staging costs no rows per workgroup (no extra
+// workgroups); otherwise each unit loads its scale bytes.
+template <int MT, int XIN, int NG>
+hipError_t launch_mt(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
+    if (G < 1 || G > NG) return hipErrorInvalidValue;
+    GroupTab<NG> with{}, without{};
+    const int64_t lds_with = plan_rows<MT, XIN, NG>(a, layers, G, num_cu, true, with);
+    const int64_t lds_without = plan_rows<MT, XIN, NG>(a, layers, G, num_cu, false, without);
+    if (lds_without < 0) return hipErrorInvalidValue;
+    if (lds_with >= 0 && with.wg_start[G] <= without.wg_start[G])
+        return launch_planned<MT, XIN, NG, true>(a, with, lds_with, stream);
+    return launch_planned<MT, XIN, NG, false>(a, without, lds_without, stream);
 }
 
 LayerDesc single_layer(const LinearArgs &a) { return LayerDesc{a.packed, a.s_rel, a.s_ch, a.cb, a.N, a.y}; }
