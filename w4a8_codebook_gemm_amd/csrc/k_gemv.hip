@@ -494,20 +494,23 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
         }
     };
 
-    // Two units went out before the prologue (they cover its latency).  From then on one unit
-    // is in flight while a unit is computed: the next unit's loads are issued first, into the
-    // slot computed last.  bu is the base of the next fetch, so slot 1 holds base bu - 128.
-    static_assert(depth<MT>() == 2, "two slots");
-    if (cur[0].valid) compute(cur[0], pa[0], pb[0], sa[0], sb[0]);
+    // kDepth units went out before the prologue (they cover its latency).  The first
+    // kDepth - 1 are computed as they are; from then on one unit is in flight while a unit
+    // is computed: the next unit's loads are issued first, into the slot computed last.  bu
+    // is the base of the next fetch, so the slot computed first in the loop body holds base
+    // bu - 128.
+#pragma unroll
+    for (int d = 0; d + 1 < kDepth; d++)
+        if (cur[d].valid) compute(cur[d], pa[d], pb[d], sa[d], sb[d]);
     while (__builtin_amdgcn_readfirstlane(bu) - kLaneGroups < units) {
-        cur[0] = make_slot();
-        fetch(cur[0], pa[0], pb[0], sa[0], sb[0]);
-        step();
-        if (cur[1].valid) compute(cur[1], pa[1], pb[1], sa[1], sb[1]);
-        cur[1] = make_slot();
-        fetch(cur[1], pa[1], pb[1], sa[1], sb[1]);
-        step();
-        if (cur[0].valid) compute(cur[0], pa[0], pb[0], sa[0], sb[0]);
+#pragma unroll
+        for (int d = 0; d < kDepth; d++) {
+            cur[d] = make_slot();
+            fetch(cur[d], pa[d], pb[d], sa[d], sb[d]);
+            step();
+            const int c = (d + kDepth - 1) % kDepth;
+            if (cur[c].valid) compute(cur[c], pa[c], pb[c], sa[c], sb[c]);
+        }
     }
     __syncthreads();
 
