@@ -28,6 +28,10 @@
 //    waves' partial tiles are summed through LDS in wave order (deterministic) and scaled
 //    by 2^(ex-8) s_ch s_x.
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
+//  * Start-up: the codebook and the workgroup's group scales are requested before the first
+//    weight loads (a request behind them waits for them to drain from HBM); the scales go
+//    straight to LDS through the buffer unit (16 B per lane), so the weight stream carries
+//    no 2-byte loads.
 #include <type_traits>
 
 #include "w4a8_internal.h"
@@ -47,6 +51,7 @@ constexpr int kMaxWaves = 16;
 // the reduction buffer holds one token tile of every wave: WAVES x NT x 1 KiB
 constexpr int kSmemBytes = kTabBytes > kMaxWaves * 4 * 1024 ? kTabBytes : kMaxWaves * 4 * 1024;
 constexpr uint32_t kOutside = 0x80000000u;  // buffer offset that reads zero
+constexpr int kSkinnyLdsMax = 160 * 1024;    // gfx950 LDS per workgroup
 // Plain loads: each instruction reads half of every 128-B line of its 16 rows and the same
 // wave reads the other half one half-block later, which must still find the line in L2.
 constexpr int kNT = 0;
@@ -54,9 +59,13 @@ constexpr int kNT = 0;
 template <int NT, int MT16>
 struct Slot {
     u32x4 pk[NT];
-    uint32_t sr[NT];
     u32x4 x[MT16][2];
 };
+
+// LDS bytes of a workgroup's staged group scales: whole 1 KiB blocks (one wave's copy)
+__host__ __device__ __forceinline__ int64_t skinny_scale_bytes(int64_t rows, int64_t grpbytes) {
+    return (rows * grpbytes + 1023) & ~(int64_t)1023;
+}
 
 __device__ __forceinline__ uint32_t pk_mul(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b));
@@ -73,7 +82,9 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
 template <int NT, int MT16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     static_assert(WAVES * NT <= kSmemBytes / 1024, "reduction buffer");
-    __shared__ __align__(16) char smem[kSmemBytes];  // pair table, then the wave reduction
+    // pair table (later the wave reduction), then the staged group scales
+    extern __shared__ __align__(16) char smem[];
+    uint8_t *ss = reinterpret_cast<uint8_t *>(smem + kSmemBytes);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -88,6 +99,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.x_q, (short)0, (int)(M * K), 0x00020000);
 
+    // the codebook (four 16-byte loads of one line), then the group scales of the
+    // workgroup's rows (nrows x K/16 contiguous bytes) copied to LDS 1 KiB per wave
+    // instruction, all before the first weight load
+    const __amdgpu_buffer_rsrc_t rs_cb = __builtin_amdgcn_make_buffer_rsrc((void *)a.cb, (short)0, kLevels * 4, 0x00020000);
+    float cbv[kLevels];
+#pragma unroll
+    for (int q = 0; q < kLevels / 4; q++) {
+        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs_cb, 16 * q, 0, 0);
+        cbv[4 * q] = __uint_as_float(c.x); cbv[4 * q + 1] = __uint_as_float(c.y);
+        cbv[4 * q + 2] = __uint_as_float(c.z); cbv[4 * q + 3] = __uint_as_float(c.w);
+    }
+    const int nsc = (int)(nrows * grpbytes / 16);
+    for (int blk = 64 * wave; blk < nsc; blk += 64 * WAVES)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (__attribute__((address_space(3))) void *)(ss + 16 * blk), 16,
+                                                 16u * (uint32_t)(blk + lane), 0, 0, kNT);
+    __builtin_amdgcn_sched_barrier(0);
+
     // this wave's share of the 128-k half-blocks: every WAVES-th one, so that at any time
     // the workgroup's waves read adjacent 64-B pieces of the same rows (long DRAM runs, and
     // both halves of each 128-B line close together)
@@ -98,12 +126,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     auto fetch = [&](int h, Slot<NT, MT16> &s) {
         const bool valid = h < h1;
         const uint32_t kb = (uint32_t)h * 64u + 16u * lq;  // packed byte within the row
-        const uint32_t ks = (uint32_t)h * 8u + 2u * lq;    // group byte within the row
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const uint32_t row = (uint32_t)(16 * t + li);
             s.pk[t] = __builtin_amdgcn_raw_buffer_load_b128(rs_p, valid ? row * rowbytes + kb : kOutside, 0, kNT);
-            s.sr[t] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, valid ? row * grpbytes + ks : kOutside, 0, kNT);
         }
 #pragma unroll
         for (int u = 0; u < MT16; u++) {
@@ -121,7 +147,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     // codebook -> fp16 pair table scaled by 2^-ex; wave w writes 16 / WAVES high nibbles
     float cmax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(a.cb[q]));
+    for (int q = 0; q < kLevels; q++) cmax = fmaxf(cmax, fabsf(cbv[q]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
     const float inv = ldexpf(1.0f, -ex);
@@ -129,13 +155,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
 #pragma unroll
     for (int hh = 0; hh < kLevels / WAVES; hh++) {
         const int hi_n = (kLevels / WAVES) * wave + hh;
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[hi_n] * inv));
+        float cbh = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kLevels; q++) cbh = q == hi_n ? cbv[q] : cbh;
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(cbh * inv));
 #pragma unroll
         for (int lo = 0; lo < kLevels; lo++) {
-            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(a.cb[lo] * inv)) | (hi << 16);
+            const uint32_t v = __builtin_bit_cast(uint16_t, (_Float16)(cbv[lo] * inv)) | (hi << 16);
             tab[(16 * hi_n + lo) * 64 + lane] = v;
         }
     }
+    // every copy to LDS of this wave is complete once at most the three ring stages' loads
+    // (issued after them) are outstanding (gfx9 s_waitcnt encoding: vmcnt in bits 3..0 and
+    // 15..14, no expcnt / lgkmcnt wait); the barrier then publishes them
+    constexpr int kRingLoads = 3 * (NT + 2 * MT16);
+    static_assert(kRingLoads < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kRingLoads & 15) | ((kRingLoads >> 4) << 14));
     __syncthreads();
 
     const uint32_t lanebase = (uint32_t)lane * 4u;
@@ -145,7 +180,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
 #pragma unroll
         for (int u = 0; u < MT16; u++) acc[t][u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](const Slot<NT, MT16> &s) {
+    auto compute = [&](int h, const Slot<NT, MT16> &s) {
         half8_t B[MT16][4];
 #pragma unroll
         for (int u = 0; u < MT16; u++) {
@@ -160,9 +195,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            // group scales as fp16 pairs, times 2^8 (exact for every e4m3 value)
-            const uint32_t s0 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)s.sr[t], 0) * 256.0f));
-            const uint32_t s1 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)s.sr[t], 1) * 256.0f));
+            // group scales of this lane's 32 values (row 16 t + li, groups 8 h + 2 lq and the
+            // next; a row past N reads stale LDS and feeds no stored output) as fp16 pairs,
+            // times 2^8 (exact for every e4m3 value)
+            const uint32_t sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grpbytes + 8u * (uint32_t)h + 2u * lq);
+            const uint32_t s0 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 0) * 256.0f));
+            const uint32_t s1 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 1) * 256.0f));
             const uint32_t sg[2] = {s0 | (s0 << 16), s1 | (s1 << 16)};
             const uint32_t pw[4] = {s.pk[t].x, s.pk[t].y, s.pk[t].z, s.pk[t].w};
 #pragma unroll
@@ -185,11 +223,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     // Fetches are unconditional (half-blocks past the range read zero) so the number of
     // loads in flight is the same on every path and each compute waits only for its own.
     for (int h = h0; h < h1; h += 3 * S) {
-        compute(R0);
+        compute(h, R0);
         fetch(h + 3 * S, R0);
-        if (h + S < h1) compute(R1);
+        if (h + S < h1) compute(h + S, R1);
         fetch(h + 4 * S, R1);
-        if (h + 2 * S < h1) compute(R2);
+        if (h + 2 * S < h1) compute(h + 2 * S, R2);
         fetch(h + 5 * S, R2);
     }
     // Wave partials are summed through LDS one token tile at a time, in wave order
@@ -239,29 +277,39 @@ template <int NT, int MT16>
 constexpr int waves_for() { return (MT16 == 1 && NT <= 3) ? 16 : (MT16 <= 2 ? 8 : 4); }
 
 template <int NT, int MT16>
-void launch_one(const LinearArgs &a, unsigned grid, hipStream_t stream) {
+hipError_t launch_one(const LinearArgs &a, unsigned grid, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
-    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), 0, stream, a);
+    const int64_t lds = kSmemBytes + skinny_scale_bytes(16 * NT, a.K / kGroup);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_skinny<NT, MT16, W>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsMax);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a);
+    return hipGetLastError();
 }
 
 template <int NT>
 hipError_t launch_nt(const LinearArgs &a, unsigned grid, hipStream_t stream) {
     switch ((a.M + 15) / 16) {
-        case 1: launch_one<NT, 1>(a, grid, stream); break;
-        case 2: launch_one<NT, 2>(a, grid, stream); break;
-        case 3: launch_one<NT, 3>(a, grid, stream); break;
-        case 4: launch_one<NT, 4>(a, grid, stream); break;
+        case 1: return launch_one<NT, 1>(a, grid, stream);
+        case 2: return launch_one<NT, 2>(a, grid, stream);
+        case 3: return launch_one<NT, 3>(a, grid, stream);
+        case 4: return launch_one<NT, 4>(a, grid, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
 bool skinny_supported(int64_t M, int64_t N, int64_t K) {
-    // 32-bit buffer offsets: token rows of x_q and a workgroup's rows of packed data
+    // 32-bit buffer offsets: token rows of x_q and a workgroup's rows of packed data; LDS:
+    // the table plus the staged group scales of kMaxTiles row tiles
     return M >= 1 && M <= 16 * kMaxTokTiles && M * K < (int64_t(1) << 31) &&
-           (int64_t)16 * kMaxTiles * (K / 2) < (int64_t(1) << 31) && N >= 1;
+           (int64_t)16 * kMaxTiles * (K / 2) < (int64_t(1) << 31) && N >= 1 &&
+           kSmemBytes + skinny_scale_bytes(16 * kMaxTiles, K / kGroup) <= kSkinnyLdsMax;
 }
 
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
