@@ -286,6 +286,28 @@ def test_mfma_skinny_full_size_sampled(w, N, K, M):
     assert_gate(y, yr, A)
 
 
+def test_mfma_skinny_long_rows(w):
+    """Rows so long that a workgroup's staged group scales leave room for fewer row tiles
+    (12304 x 32768 wants four 16-row tiles per workgroup; three fit beside the table).  The
+    layer is made of random bytes in the format's ranges rather than quantised (the product
+    is defined by the four tensors alone); sampled rows against the oracle's product."""
+    N, K, M = 12304, 32768, 8
+    say(f"mfma_skinny long rows N={N} K={K} M={M}")
+    g = np.random.default_rng(5)
+    packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
+    s_rel = g.integers(0x20, 0x39, size=(N, K // 16), dtype=np.uint8)  # e4m3 codes in [2^-4, 1]
+    s_ch = (0.01 + 0.02 * g.random(N)).astype(np.float32)
+    cb = np.sort(g.standard_normal(16)).astype(np.float32)
+    _, xq, sx = oracle_acts(M, K, 9, 2)
+    L = w.QuantizedLinear(gpu(packed), gpu(s_rel), gpu(s_ch), gpu(cb))
+    y = w.linear(gpu(xq), gpu(sx), L, algo=w.ALGO_MFMA_SKINNY)
+    torch.cuda.synchronize()
+    rows = sample(N, 256, 11)
+    y = y.float().cpu().numpy().astype(np.float64)[:, rows]
+    yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb, rows, None)
+    assert_gate(y, yr, A)
+
+
 @pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16", "mfma_skinny"])
 def test_bf16_output(w, algo):
     a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3, "mfma_skinny": 4}[algo]

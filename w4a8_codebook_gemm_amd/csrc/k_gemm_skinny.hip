@@ -309,15 +309,17 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K) {
     // the table plus the staged group scales of kMaxTiles row tiles
     return M >= 1 && M <= 16 * kMaxTokTiles && M * K < (int64_t(1) << 31) &&
            (int64_t)16 * kMaxTiles * (K / 2) < (int64_t(1) << 31) && N >= 1 &&
-           kSmemBytes + skinny_scale_bytes(16 * kMaxTiles, K / kGroup) <= kSkinnyLdsMax;
+           kSmemBytes + skinny_scale_bytes(16, K / kGroup) <= kSkinnyLdsMax;
 }
 
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
     if (!skinny_supported(a.M, a.N, a.K)) return hipErrorInvalidValue;
     // tiles per workgroup: enough to give every CU one workgroup, at most kMaxTiles
     const int64_t tiles = (a.N + 15) / 16;
+    // (fewer for long rows: the staged scales of a workgroup's rows must fit in LDS)
     int64_t nt = (tiles + num_cu - 1) / num_cu;
     if (nt > kMaxTiles) nt = kMaxTiles;
+    while (nt > 1 && kSmemBytes + skinny_scale_bytes(16 * nt, a.K / kGroup) > kSkinnyLdsMax) nt--;
     if (nt < 1) nt = 1;
     const unsigned grid = (unsigned)((tiles + nt - 1) / nt);
     switch (nt) {
