@@ -47,6 +47,8 @@ def lib():
         L.orc_codebook_i8.argtypes = [P, P, P]
         L.orc_linear_i8_ref.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i64, P, i64,
                                         P, P, P]
+        L.orc_rq_table.argtypes = [P, P]
+        L.orc_linear_rq_ref.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i64, P, i64, P]
         L.orc_quantize_w8.argtypes = [P, i64, i64, P, P]
         L.orc_linear_w8_ref.argtypes = [P, P, i64, i64, P, P, i64, P]
         _lib = L
@@ -198,6 +200,29 @@ def linear_i8_ref(xq, sx, packed, s_rel, s_ch, cb, rows=None, toks=None, want_p=
                             _p(_c(cb, np.float32)), N, _p(rows), nrow, _p(toks), ntok,
                             _p(y), _p(A), _p(P))
     return (y, A, P) if want_p else (y, A)
+
+
+def rq_table(cb) -> np.ndarray:
+    """Requantised int8 weight table t [256 e4m3 codes, 16 levels]."""
+    cb = _c(cb, np.float32)
+    t = np.empty((256, 16), dtype=np.int8)
+    lib().orc_rq_table(_p(cb), _p(t))
+    return t
+
+
+def linear_rq_ref(xq, sx, packed, s_rel, s_ch, cb, rows=None, toks=None):
+    """Product on requantised int8 weights: y fp32 [ntok, nrow], exactly as defined."""
+    xq = _c(xq, np.int8)
+    M, K = xq.shape
+    packed = _c(packed, np.int8)
+    N = packed.shape[0]
+    rows, nrow = _subset(rows, N)
+    toks, ntok = _subset(toks, M)
+    y = np.empty((ntok, nrow), dtype=np.float32)
+    lib().orc_linear_rq_ref(_p(xq), _p(_c(sx, np.float32)), M, K, _p(packed),
+                            _p(_c(s_rel, np.uint8)), _p(_c(s_ch, np.float32)),
+                            _p(_c(cb, np.float32)), N, _p(rows), nrow, _p(toks), ntok, _p(y))
+    return y
 
 
 def quantize_w8(W):

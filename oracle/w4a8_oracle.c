@@ -433,6 +433,72 @@ void orc_linear_i8_ref(const int8_t *xq, const float *sx, int64_t M, int64_t K,
     }
 }
 
+/* ------------------------------------------------------------------------------------
+ * Requantised int8 weights: the second reading of the int8 execution.  [card A "Why this
+ * exists": the W4A8 layer runs on the same int8 GEMM path as INT8 with a codebook
+ * dequantisation step added.]  Where orc_linear_i8_ref keeps the group scale outside the
+ * integer sum (one fold per 16 values), this reading decodes each weight with its group
+ * scale and rounds it to int8 on one per-tensor step, so a single integer sum covers the
+ * whole row and the scales enter once:
+ *   s_cb     = max_j |cb[j]| / 127                                   (fp32, as orc_codebook_i8)
+ *   t[c][j]  = rint(fl(dec(c) * cb[j]) / s_cb)  for each e4m3 code c   (fp32 product, then fp32
+ *              quotient, ties to even; clamped to [-127, 127]; 0 where the quotient is NaN)
+ *   q[r,k]   = t[s_rel[r,k/16]][idx[r,k]]
+ *   acc[m,r] = sum_k x_q[m,k] q[r,k]                                 (exact integer)
+ *   y[m,r]   = fl(fl(fl(acc) * fl(s_ch[r] * s_cb)) * s_x[m])          (fp32, in this order)
+ * No value is clamped when every |dec(s_rel)| <= 1, which orc_quantize_weight guarantees
+ * (the group that holds a row's largest magnitude has relative scale 1).  The rounding
+ * step is s_cb in units of s_ch[r], so |q s_cb - dec cb| <= s_cb / 2 for each weight.
+ * ------------------------------------------------------------------------------------ */
+void orc_rq_table(const float *cb, int8_t *tab /* [256][16] */) {
+    float mx = 0.0f;
+    for (int j = 0; j < LEVELS; j++) mx = fmaxf(mx, fabsf(cb[j]));
+    const float s = mx / 127.0f;
+    for (int c = 0; c < 256; c++) {
+        const float d = (float)orc_e4m3_decode((uint8_t)c);
+        for (int j = 0; j < LEVELS; j++) {
+            const float prod = d * cb[j];
+            const float v = prod / s;
+            float qv = 0.0f;
+            if (!isnan(v)) {
+                qv = rintf(v);
+                qv = qv > 127.0f ? 127.0f : (qv < -127.0f ? -127.0f : qv);
+            }
+            tab[c * LEVELS + j] = (int8_t)qv;
+        }
+    }
+}
+
+void orc_linear_rq_ref(const int8_t *xq, const float *sx, int64_t M, int64_t K,
+                       const int8_t *packed, const uint8_t *s_rel, const float *s_ch,
+                       const float *cb, int64_t N, const int64_t *rows, int64_t nrow,
+                       const int64_t *toks, int64_t ntok, float *y) {
+    if (!rows) nrow = N;
+    if (!toks) ntok = M;
+    const int64_t G = K / GRP;
+    int8_t tab[256 * LEVELS];
+    orc_rq_table(cb, tab);
+    float mx = 0.0f;
+    for (int j = 0; j < LEVELS; j++) mx = fmaxf(mx, fabsf(cb[j]));
+    const float s_cb = mx / 127.0f;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < nrow; ri++) {
+        int64_t r = rows ? rows[ri] : ri;
+        int8_t *q = (int8_t *)malloc((size_t)K);
+        for (int64_t k = 0; k < K; k++)
+            q[k] = tab[s_rel[r * G + k / GRP] * LEVELS + unpack_idx(packed + r * (K / 2), k)];
+        const float sw = s_ch[r] * s_cb;
+        for (int64_t ti = 0; ti < ntok; ti++) {
+            int64_t m = toks ? toks[ti] : ti;
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; k++) acc += (int64_t)xq[m * K + k] * (int64_t)q[k];
+            const float t = (float)acc * sw;
+            y[ti * nrow + ri] = t * sx[m];
+        }
+        free(q);
+    }
+}
+
 /* ---------------------------------------------------------------- W8A8 comparator
  * The INT8 ConvRot format the W4A8 layer is weighed against [card A, "Why this exists": an
  * INT8 ConvRot build of the same model, about twice the weight bytes].  The cards give no

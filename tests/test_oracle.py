@@ -437,6 +437,79 @@ def test_linear_i8_partials_exact_and_codebook_properties():
     assert np.all(np.abs(y8 - y8n) <= 1e-12 * A8)
 
 
+# Integer codebook with max |level| = 127, so s_cb = 1 exactly and the table entries below
+# are hand values: t[c][j] = level_j * dec(c) rounded half to even, clamped to +-127.
+RQ_CB = np.array([-127, -64, -5, -3, -1, 0, 1, 3, 5, 7, 9, 11, 50, 64, 100, 127], np.float32)
+RQ_HAND = {
+    0x38: [-127, -64, -5, -3, -1, 0, 1, 3, 5, 7, 9, 11, 50, 64, 100, 127],       # 1.0
+    0x30: [-64, -32, -2, -2, 0, 0, 0, 2, 2, 4, 4, 6, 25, 32, 50, 64],             # 0.5
+    0x28: [-32, -16, -1, -1, 0, 0, 0, 1, 1, 2, 2, 3, 12, 16, 25, 32],             # 0.25
+    0x34: [-95, -48, -4, -2, -1, 0, 1, 2, 4, 5, 7, 8, 38, 48, 75, 95],            # 0.75
+    0x40: [-127, -127, -10, -6, -2, 0, 2, 6, 10, 14, 18, 22, 100, 127, 127, 127], # 2.0: clamps
+    0xB8: [127, 64, 5, 3, 1, 0, -1, -3, -5, -7, -9, -11, -50, -64, -100, -127],   # -1.0
+    0x00: [0] * 16,                                                               # +0
+    0x7F: [0] * 16, 0xFF: [0] * 16,                                               # NaN codes
+}
+
+
+def test_rq_table_hand_values_and_rounding_bound():
+    t = O.rq_table(RQ_CB)
+    for c, want in RQ_HAND.items():
+        assert t[c].tolist() == want, hex(c)
+    # a fitted codebook: the row of scale 1 is the separately pinned int8 codebook, and every
+    # code with |dec| <= 1 rounds each decoded level to the nearest multiple of s_cb
+    W, x, q, xq, sx = _layer(32, 512, 3, 14)
+    s_cb, cbi8 = O.codebook_i8(q["cb"])
+    t = O.rq_table(q["cb"])
+    assert np.array_equal(t[0x38], cbi8)
+    dec = e4m3_torch_decode(np.arange(256))
+    for c in range(256):
+        if np.isnan(dec[c]) or abs(dec[c]) > 1:
+            continue
+        exact = dec[c] * q["cb"].astype(np.float64)
+        assert np.abs(t[c]).max() <= 127
+        assert np.all(np.abs(t[c] * np.float64(s_cb) - exact) <= s_cb / 2 * (1 + 1e-6) + 1e-12), hex(c)
+
+
+def test_rq_product_assembly_exact_case_and_error_bound():
+    W, x, q, xq, sx = _layer(40, 768, 5, 15)
+    N, K, M = 40, 768, 5
+    yq = O.linear_rq_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    # assembly: per-weight table lookup (nibble order, group k/16), exact integer matmul,
+    # the three fp32 roundings of the epilogue
+    t = O.rq_table(q["cb"])
+    s_cb, _ = O.codebook_i8(q["cb"])
+    idx = np.empty((N, K), np.int64)
+    idx[:, 0::2] = q["packed"].view(np.uint8) & 15
+    idx[:, 1::2] = q["packed"].view(np.uint8) >> 4
+    code = np.repeat(q["s_rel"].astype(np.int64), 16, axis=1)
+    wq = t[code, idx].astype(np.int64)
+    acc = xq.astype(np.int64) @ wq.T
+    sw = q["s_ch"] * np.float32(s_cb)
+    ye = (acc.astype(np.float32) * sw[None, :]) * sx[:, None]
+    assert ye.dtype == np.float32 and np.array_equal(yq.view(np.uint32), ye.view(np.uint32))
+    # against the exact product: the rounding of each weight is at most s_cb / 2 in units of
+    # the row scale (every group scale the quantiser writes is at most 1)
+    y, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    assert np.all(e4m3_torch_decode(q["s_rel"]) <= 1)
+    step = (np.abs(sx.astype(np.float64))[:, None] * q["s_ch"].astype(np.float64)[None, :] * s_cb / 2
+            * np.abs(xq.astype(np.float64)).sum(1)[:, None])
+    assert np.all(np.abs(yq - y) <= step * (1 + 1e-5) + 8 * U32 * A)
+    print(f"rq vs exact: max |dy| / (4e-3 A) = {(np.abs(yq - y) / (4e-3 * A)).max():.4f}")
+    # subsets address the same outputs
+    rows, toks = np.array([39, 0, 17]), np.array([4, 1])
+    ys = O.linear_rq_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, toks)
+    assert np.array_equal(ys, yq[np.ix_(toks, rows)])
+    # a codebook on the integer grid with unit group scales: requantisation is exact and the
+    # result is the exact product up to the epilogue's roundings
+    cbi = np.sort(RQ_CB)
+    s1 = np.full_like(q["s_rel"], 0x38)
+    yi = O.linear_rq_ref(xq, sx, q["packed"], s1, q["s_ch"], cbi)
+    yr, Ar = O.linear_ref(xq, sx, q["packed"], s1, q["s_ch"], cbi)
+    assert np.all(np.abs(yi - yr) <= 3 * U32 * np.abs(yr))
+    assert np.abs(yr).max() > 0
+
+
 def test_plausibility_against_unquantised_product():
     W, x, q, xq, sx = _layer(256, 512, 4, 0)
     y, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
