@@ -407,14 +407,15 @@ def prefill(w, torch, S, shapes, M=2048):
     for (n, k) in shapes:
         xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
         y = torch.empty((M, n), dtype=torch.float32, device="cuda")
-        for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16")):
+        for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16"), (w.ALGO_MFMA_RQ, "mfma_rq")):
             g = make_graph(torch, lambda: [w.linear(xq, sx, pl[(n, k)][c], out=y, algo=algo) for c in range(2)])
             t = time_graph(torch, g, 10) / 2
             tops = 2.0 * M * n * k / t / 1e12
             pre[f"{n}x{k}/{name}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
             log(f"prefill {name} M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
     summary = {}
-    for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s")):
+    for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s"),
+                             ("mfma_rq", INT8_PEAK_TOPS, "TOP/s")):
         mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
         summary[name] = dict(tops=round(mean, 1), roofline=dict(
             bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
@@ -495,7 +496,9 @@ def w8a8(w, torch, S, shapes, w4_gemv, w4_unfused_us, w4_prefill, M=2048):
     out["prefill"] = dict(tokens=M, shapes=pre, tops=round(mean, 1), roofline=dict(
         bound="mfma", achieved=round(mean, 1), peak=INT8_PEAK_TOPS, unit="TOP/s", frac=round(mean / INT8_PEAK_TOPS, 4)))
     if w4_prefill:
-        out["prefill"]["w4a8_best_tops"] = max(w4_prefill["mfma_i8"]["tops"], w4_prefill["mfma_f16"]["tops"])
+        best = max(("mfma_i8", "mfma_f16", "mfma_rq"), key=lambda r: w4_prefill[r]["tops"])
+        out["prefill"]["w4a8_best_tops"] = w4_prefill[best]["tops"]
+        out["prefill"]["w4a8_best_route"] = best
     del layers
     torch.cuda.empty_cache()
     out["model"] = w8a8_model(w, torch, S)
@@ -579,7 +582,7 @@ def pmc_pass(w, torch, S, shapes):
     for (n, k), L in ((S.MLP_GATE_UP, blocks[0]["gate"]), (S.MLP_DOWN, blocks[0]["down"])):
         xq, sx = w.prepare_activation(torch.from_numpy(S.activations(2048, k, seed=0)).cuda())
         y = torch.empty((2048, n), dtype=torch.float32, device="cuda")
-        for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16):
+        for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ):
             w.linear(xq, sx, L, out=y, algo=algo)
     torch.cuda.synchronize()
     log("pmc pass done")

@@ -70,8 +70,14 @@ typedef enum {
                                  per-16 partials, fp32 group-scale fold */
     W4A8_ALGO_MFMA_F16 = 3,   /* f16 MFMA on decoded weights (codebook x group scale in f16),
                                  128 x 256 tiles (prefill) */
-    W4A8_ALGO_MFMA_SKINNY = 4 /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
+    W4A8_ALGO_MFMA_SKINNY = 4, /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
                                  16-row weight tiles streamed once, M*K < 2^31 */
+    W4A8_ALGO_MFMA_RQ = 5     /* full-rate int8 MFMA on requantised weights (prefill):
+                                 q = rint(dec(s_rel) * codebook[idx] / s_cb), s_cb = max|codebook|
+                                 / 127, clamped to +-127, one int32 sum per output,
+                                 y = ((float)sum * (s_channel * s_cb)) * s_x; K <= 131072.
+                                 Weight rounding to the step s_cb is the only approximation
+                                 (card A "Why this exists": int8 GEMM + dequantisation step) */
 } w4a8_algo;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -147,7 +153,9 @@ W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t
 
 /* As w4a8_linear with an explicit kernel choice (w4a8_algo).  W4A8_ALGO_GEMV returns
  * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960), W4A8_ALGO_MFMA_SKINNY outside
- * its range (M <= 64, M*K < 2^31, 40*K < 2^31). */
+ * its range (M <= 64, M*K < 2^31, 40*K < 2^31), W4A8_ALGO_MFMA_RQ for K > 131072 (the
+ * int32 sum must stay exact) or more than 2^31 - 1 tiles of 256 tokens x 192 rows.  An
+ * unknown algorithm code returns W4A8_ERR_DTYPE. */
 W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,

@@ -80,7 +80,8 @@ def test_linear_validation(L):
         assert lin(L, ptrs={k: MIS}) == 4
     assert lin(L, M=8, K=5120, algo=w.ALGO_GEMV) == 2  # outside the GEMV's range
     assert lin(L, M=65, K=512, algo=w.ALGO_MFMA_SKINNY) == 2  # outside the skinny kernel's
-    assert lin(L, algo=5) == 3
+    assert lin(L, algo=6) == 3
+    assert lin(L, M=4, K=131328, algo=w.ALGO_MFMA_RQ) == 2  # the int32 sum would not be exact
     assert L.w4a8_linear(0, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == 1
 
 

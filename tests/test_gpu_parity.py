@@ -265,6 +265,70 @@ def test_mfma_f16_full_size_sampled(w, N, K):
     assert_gate(y, yr, A)
 
 
+# Requantised int8 weights: the kernel and the oracle take the same integer decisions (the
+# table of rounded group-scaled levels, exact int32 sums) and the same three fp32 roundings,
+# so the outputs are compared bit for bit; the gate against the exact product is the
+# tolerance study of this reading.
+def run_rq(w, N, K, M, rows=None, toks=None, out_dtype=torch.float32, seed=0, layer=None):
+    if layer is None:
+        _, q = oracle_layer(N, K, seed)
+        layer = (q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    _, xq, sx = oracle_acts(M, K, seed, 2)
+    L = w.QuantizedLinear(*(gpu(t) for t in layer))
+    y = w.linear(gpu(xq), gpu(sx), L, out_dtype=out_dtype, algo=w.ALGO_MFMA_RQ)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    rr = np.arange(N) if rows is None else rows
+    tt = np.arange(M) if toks is None else toks
+    y = y[np.ix_(tt, rr)]
+    yq = O.linear_rq_ref(xq, sx, *layer, rows, toks)
+    return y, yq, (xq, sx, layer)
+
+
+@pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (512, 256, 257),
+                                   (17, 5120, 3), (385, 1280, 600), (193, 256, 65), (1000, 2048, 513)])
+def test_mfma_rq_parity(w, N, K, M):
+    say(f"mfma_rq N={N} K={K} M={M}")
+    y, yq, (xq, sx, layer) = run_rq(w, N, K, M)
+    assert np.array_equal(y.view(np.uint32), yq.view(np.uint32))
+    yr, A = O.linear_ref(xq, sx, *layer)
+    assert_gate(y.astype(np.float64), yr, A)
+
+
+@pytest.mark.parametrize("N,K", [S.MLP_GATE_UP, S.MLP_DOWN])
+def test_mfma_rq_full_size_sampled(w, N, K):
+    M = 2048
+    say(f"mfma_rq full N={N} K={K} M={M}")
+    rows, toks = sample(N, 384, N), sample(M, 48, M + 1)
+    y, yq, (xq, sx, layer) = run_rq(w, N, K, M, rows=rows, toks=toks)
+    assert np.array_equal(y.view(np.uint32), yq.view(np.uint32))
+    yr, A = O.linear_ref(xq, sx, *layer, rows, toks)
+    assert_gate(y.astype(np.float64), yr, A)
+
+
+def test_mfma_rq_every_scale_code(w):
+    """Random layer bytes with group-scale codes over the whole e4m3 range, the NaN codes and
+    scales above 1 (whose levels clamp at +-127) included: the clamping and NaN rules of the
+    table, bit for bit."""
+    N, K, M = 300, 1024, 70
+    g = np.random.default_rng(8)
+    packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
+    s_rel = g.integers(0, 256, size=(N, K // 16), dtype=np.uint8)
+    s_ch = (0.01 + 0.02 * g.random(N)).astype(np.float32)
+    cb = np.sort(g.standard_normal(16)).astype(np.float32)
+    say(f"mfma_rq all codes N={N} K={K} M={M}")
+    y, yq, _ = run_rq(w, N, K, M, layer=(packed, s_rel, s_ch, cb))
+    assert np.array_equal(y.view(np.uint32), yq.view(np.uint32))
+
+
+def test_mfma_rq_bf16_output(w):
+    N, K, M = 385, 768, 300
+    say(f"mfma_rq bf16 N={N} K={K} M={M}")
+    y, yq, _ = run_rq(w, N, K, M, out_dtype=torch.bfloat16)
+    want = torch.from_numpy(yq).to(torch.bfloat16).float().numpy()   # round to nearest even
+    assert np.array_equal(y.view(np.uint32), want.view(np.uint32))
+
+
 # (N, K, M): 16-row tiles per workgroup 1..5 (N = 2048, 5120, 10000, 15360, 17408 on 256 CUs),
 # token tiles 1..4, ragged N and M, K = 256 (waves with no K range)
 SKINNY_CASES = [(256, 512, 3), (300, 768, 17), (1001, 1024, 33), (17, 5120, 64), (64, 256, 5),
@@ -316,8 +380,8 @@ def test_bf16_output(w, algo):
     assert_gate(y, yr, A, extra=2.0 ** -8 * np.abs(yr))
 
 
-@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (4, 3), (4, 64), (0, 1), (0, 8),
-                                    (0, 300)])
+@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (4, 3), (4, 64), (5, 300), (0, 1),
+                                    (0, 8), (0, 300)])
 def test_deterministic_and_auto(w, algo, M):
     say(f"determinism algo={algo} M={M}")
     N, K = 512, 1024

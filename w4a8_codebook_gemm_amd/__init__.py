@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
 F32, BF16 = 0, 1
-ALGO_AUTO, ALGO_GEMV, ALGO_MFMA_I8, ALGO_MFMA_F16, ALGO_MFMA_SKINNY = 0, 1, 2, 3, 4
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA_I8, ALGO_MFMA_F16, ALGO_MFMA_SKINNY, ALGO_MFMA_RQ = 0, 1, 2, 3, 4, 5
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",

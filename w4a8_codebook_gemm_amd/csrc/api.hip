@@ -124,10 +124,11 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     if (st != W4A8_OK) return st;
     if (algo == W4A8_ALGO_AUTO) algo = pick(M, N, K);
     if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8 && algo != W4A8_ALGO_MFMA_F16 &&
-        algo != W4A8_ALGO_MFMA_SKINNY)
+        algo != W4A8_ALGO_MFMA_SKINNY && algo != W4A8_ALGO_MFMA_RQ)
         return W4A8_ERR_DTYPE;
     if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
     if (algo == W4A8_ALGO_MFMA_SKINNY && !w4a8::skinny_supported(M, N, K)) return W4A8_ERR_SHAPE;
+    if (algo == W4A8_ALGO_MFMA_RQ && !w4a8::gemm_rq_supported(M, N, K)) return W4A8_ERR_SHAPE;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A8_OK) return st;
@@ -139,6 +140,7 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
         case W4A8_ALGO_GEMV: e = w4a8::launch_gemv(a, num_cu, s); break;
         case W4A8_ALGO_MFMA_I8: e = w4a8::launch_gemm_i8(a, s); break;
         case W4A8_ALGO_MFMA_SKINNY: e = w4a8::launch_gemm_skinny(a, num_cu, s); break;
+        case W4A8_ALGO_MFMA_RQ: e = w4a8::launch_gemm_rq(a, s); break;
         default: e = w4a8::launch_gemm_f16(a, s); break;
     }
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;

@@ -42,27 +42,6 @@ constexpr int JB = BN / 64;                    // 32-row weight blocks per wave
 constexpr int kPitch = BK + 8;                 // bytes per LDS row
 constexpr int kXStage = BM * kPitch, kBStage = BN * kPitch, kSStage = (BK / kGroup) * BN;
 
-struct CbI8 {
-    uint32_t t[4];  // cb_i8[0..15] as bytes
-};
-
-// four 4-bit indices (one per byte) -> the four int8 levels
-__device__ __forceinline__ uint32_t lookup4(const CbI8 &c, uint32_t idx4) {
-    const uint32_t sel = idx4 & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(c.t[1], c.t[0], sel);
-    const uint32_t hi = __builtin_amdgcn_perm(c.t[3], c.t[2], sel);
-    const uint32_t msel = ((idx4 >> 3) & 0x01010101u) | 0x0C0C0C0Cu;  // 0x0C -> 0x00, 0x0D -> 0xFF
-    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, msel);
-    return (mask & hi) | (~mask & lo);
-}
-
-// one packed dword (k = 0..7: low nibble of byte b is k = 2b) -> 8 int8 in k order
-__device__ __forceinline__ uint2 decode8(const CbI8 &c, uint32_t w) {
-    const uint32_t even = lookup4(c, w & 0x0F0F0F0Fu);         // k = 0, 2, 4, 6
-    const uint32_t odd = lookup4(c, (w >> 4) & 0x0F0F0F0Fu);   // k = 1, 3, 5, 7
-    return make_uint2(__builtin_amdgcn_perm(odd, even, 0x05010400u), __builtin_amdgcn_perm(odd, even, 0x07030602u));
-}
-
 struct Stage {
     uint4 x0, x1;   // 32 activation bytes of token xr
     uint4 p;        // 32 packed indices of weight row pr (two groups)

@@ -233,6 +233,29 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
 
+// ---------------------------------------------------------------- int8 level tables
+// Sixteen int8 levels, one per 4-bit index, looked up with byte permutes.
+struct CbI8 {
+    uint32_t t[4];  // the 16 levels as bytes, level j in byte j % 4 of t[j / 4]
+};
+
+// four 4-bit indices (one per byte) -> the four int8 levels
+__device__ __forceinline__ uint32_t lookup4(const CbI8 &c, uint32_t idx4) {
+    const uint32_t sel = idx4 & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(c.t[1], c.t[0], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(c.t[3], c.t[2], sel);
+    const uint32_t msel = ((idx4 >> 3) & 0x01010101u) | 0x0C0C0C0Cu;  // 0x0C -> 0x00, 0x0D -> 0xFF
+    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, msel);
+    return (mask & hi) | (~mask & lo);
+}
+
+// one packed dword (k = 0..7: low nibble of byte b is k = 2b) -> 8 int8 in k order
+__device__ __forceinline__ uint2 decode8(const CbI8 &c, uint32_t w) {
+    const uint32_t even = lookup4(c, w & 0x0F0F0F0Fu);         // k = 0, 2, 4, 6
+    const uint32_t odd = lookup4(c, (w >> 4) & 0x0F0F0F0Fu);   // k = 1, 3, 5, 7
+    return make_uint2(__builtin_amdgcn_perm(odd, even, 0x05010400u), __builtin_amdgcn_perm(odd, even, 0x07030602u));
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
 hipError_t launch_prepare(const void *x, int x_bf16, int64_t M, int64_t K, int8_t *x_q,
@@ -278,6 +301,8 @@ hipError_t launch_gemv_fused_multi(const LinearArgs &a, const LayerDesc *layers,
                                    hipStream_t stream);
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
+bool gemm_rq_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_rq(const LinearArgs &a, hipStream_t stream);
 bool skinny_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream);
 
