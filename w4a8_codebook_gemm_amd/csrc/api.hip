@@ -252,7 +252,8 @@ int w4a8_w8a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, 
     if (algo == W4A8_ALGO_AUTO) algo = w4a8::w8_gemv_supported(M, K) ? W4A8_ALGO_GEMV : W4A8_ALGO_MFMA_I8;
     if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8) return W4A8_ERR_DTYPE;
     if (algo == W4A8_ALGO_GEMV && !w4a8::w8_gemv_supported(M, K)) return W4A8_ERR_SHAPE;
-    if (algo == W4A8_ALGO_MFMA_I8 && ((M + 127) / 128) * ((N + 127) / 128) > (int64_t(1) << 31) - 1)
+    // the tile count must fit the grid
+    if (algo == W4A8_ALGO_MFMA_I8 && ((M + 255) / 256) * ((N + 191) / 192) > (int64_t(1) << 31) - 1)
         return W4A8_ERR_SHAPE;
     int num_cu = 0;
     int st = current_device(&num_cu);

@@ -18,14 +18,21 @@
 // the step (at most s_cb / 2 in units of the row scale when every |dec(s_rel)| <= 1).
 //
 // No group boundary falls inside the integer sum, so the kernel runs the full-rate
-// v_mfma_i32_32x32x32_i8.  Tile and schedule follow the W8A8 comparator's GEMM: 256 tokens
-// x 192 weight rows per 512-thread workgroup (4 x 2 waves of 64 x 96), one workgroup per
-// CU, 64-byte K stages double-buffered through LDS with the global loads four stages ahead
-// in a ring of register stages, int32 accumulation over all of K.  Per stage each thread
-// copies 32 activation bytes and decodes one group of 16 weights (8 packed bytes and one
-// scale byte; threads < 256 a second group of row + 128), which spreads the decode evenly
-// over the four SIMDs.  Tiles are numbered so that each XCD works through a contiguous run
-// of them, token tiles fastest.
+// v_mfma_i32_32x32x32_i8.  Tile: 256 tokens x 192 weight rows per 512-thread workgroup
+// (4 x 2 waves of 64 x 96), one workgroup per CU, int32 accumulation over all of K.
+//  * K advances in stages of 128, double-buffered through LDS in 144-byte rows (the 16
+//    rows one phase of a 16-byte fragment read touches start on distinct bank quads).
+//  * Every global load covers whole 128-byte lines: eight lanes per row, 16 activation
+//    bytes or one group (8 packed bytes and its scale byte) per lane, eight rows per load.
+//    Each thread copies four activation chunks and decodes three groups per stage, the
+//    same for every wave.  A stage's loads are issued one stage ahead into a ring of two
+//    register stages.
+//  * Each stage is scheduled by hand: the fragments of 32-k step t + 1 are read while step
+//    t's six MFMAs run, and the next stage's decode (table read, lookups, LDS store) is
+//    spread between them, so neither the LDS latency nor the decode stalls the MFMA issue.
+// Tiles are numbered so that each XCD works through a contiguous run of them, token tiles
+// fastest.
+
 #include <type_traits>
 
 #include "w4a8_internal.h"
@@ -36,28 +43,31 @@ namespace {
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 
-constexpr int GM = 256, GN = 192, GK = 64;  // tile: tokens x weight rows x K per stage
+constexpr int GM = 256, GN = 192, GK = 128;  // tile: tokens x weight rows x K per stage
 constexpr int kThreads = 512;
-constexpr int GJB = GN / 64;                // 32-row weight blocks per wave
-// 80-byte LDS rows: the 16 rows one 16-lane phase of a 16-byte fragment read touches start
-// at distinct multiples of 16 bytes modulo 256, i.e. on disjoint bank quads
+constexpr int GJB = GN / 64;                 // 32-row weight blocks per wave
 constexpr int kPitch = GK + 16;
 constexpr int kXSt = GM * kPitch, kWSt = GN * kPitch;
+constexpr int XJ = GM / 64, WJ = GN / 64;    // staged rows per thread: 4 activation, 3 weight
 constexpr int kCodes = 256;
 
 struct RStage {
-    int4v x0, x1;      // 32 activation bytes of token xr
-    uint2 p0, p1;      // 16 packed indices (one group) of rows wr and wr + 128
-    uint32_t s0, s1;   // their e4m3 group scales
+    int4v x[XJ];      // 16 activation bytes of rows sr + 64 j
+    uint2 p[WJ];      // the packed group (16 indices) of weight rows sr + 64 j
+    uint32_t s[WJ];   // their e4m3 group scales
+};
+
+struct Frag {
+    int4v A[2], B[GJB];
 };
 
 template <int J>
 using RIC = std::integral_constant<int, J>;
 
-// two waves per SIMD: the accumulators and the register ring need up to 256 registers
+// two waves per SIMD: the accumulators, two fragment sets and the register ring
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_rq(LinearArgs a, int tiles_m, int tiles) {
-    __shared__ __align__(16) int8_t xs[2][kXSt];
-    __shared__ __align__(16) int8_t ws[2][kWSt];
+    __shared__ __align__(16) int8_t xs[2 * kXSt];
+    __shared__ __align__(16) int8_t ws[2 * kWSt];
     __shared__ __align__(16) uint8_t tab[kCodes * kLevels];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -68,37 +78,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_rq(LinearArgs a, int tiles
     const int t = xcd * q + min(xcd, rem) + slot;
     const int64_t m0 = (int64_t)(t % tiles_m) * GM, n0 = (int64_t)(t / tiles_m) * GN;
 
-    // ---- staging roles (every load is issued before the table is built)
-    static_assert(GN > 128 && GN <= 256 && kThreads == 512, "weight staging covers 128 + (GN - 128) rows");
-    const int xr = tid >> 1, xh = tid & 1;
-    const int wr = tid >> 2, wq = tid & 3;
-    const bool w1st = wr < GN - 128;               // wave-uniform: 4 (GN - 128) is a multiple of 64
-    const int64_t r0 = min<int64_t>(n0 + wr, N - 1);
-    const int64_t r1 = min<int64_t>(n0 + (w1st ? 128 + wr : GN - 1), N - 1);
-    const int8_t *xp = a.x_q + min<int64_t>(m0 + xr, M - 1) * K + 32 * xh;
-    const int8_t *pp0 = a.packed + r0 * (K / 2) + 8 * wq;
-    const int8_t *pp1 = a.packed + r1 * (K / 2) + 8 * wq;
-    const uint8_t *sp0 = a.s_rel + r0 * (K / kGroup) + wq;
-    const uint8_t *sp1 = a.s_rel + r1 * (K / kGroup) + wq;
-    const int nk = (int)(K / GK);
+    // ---- staging roles: rows sr + 64 j, 16-byte chunk / group sc of the stage.  Rows past
+    // M or N re-read the last valid row: they feed only outputs that are never stored.
+    const int sr = tid >> 3, sc = tid & 7;
+    const int8_t *xp[XJ];
+    const int8_t *pp[WJ];
+    const uint8_t *spp[WJ];
+#pragma unroll
+    for (int j = 0; j < XJ; j++) xp[j] = a.x_q + min<int64_t>(m0 + sr + 64 * j, M - 1) * K + 16 * sc;
+#pragma unroll
+    for (int j = 0; j < WJ; j++) {
+        const int64_t r = min<int64_t>(n0 + sr + 64 * j, N - 1);
+        pp[j] = a.packed + r * (K / 2) + 8 * sc;
+        spp[j] = a.s_rel + r * (K / kGroup) + sc;
+    }
+    const int nk = (int)(K / GK);  // even: K is a multiple of 256
 
     // every stage's loads are issued unconditionally (stages past the end re-read the last
-    // one) so that the in-order load counter lets a store wait for its own stage only
+    // one) so that the in-order load counter lets a decode wait for its own stage only
     auto gload = [&](int kt, RStage &st) {
         const int64_t k = kt < nk ? kt : nk - 1;
-        st.x0 = *reinterpret_cast<const int4v *>(xp + k * GK);
-        st.x1 = *reinterpret_cast<const int4v *>(xp + k * GK + 16);
-        st.p0 = *reinterpret_cast<const uint2 *>(pp0 + k * (GK / 2));
-        st.p1 = *reinterpret_cast<const uint2 *>(pp1 + k * (GK / 2));
-        st.s0 = sp0[k * (GK / kGroup)];
-        st.s1 = sp1[k * (GK / kGroup)];
+#pragma unroll
+        for (int j = 0; j < XJ; j++) st.x[j] = *reinterpret_cast<const int4v *>(xp[j] + k * GK);
+#pragma unroll
+        for (int j = 0; j < WJ; j++) st.p[j] = *reinterpret_cast<const uint2 *>(pp[j] + k * (GK / 2));
+#pragma unroll
+        for (int j = 0; j < WJ; j++) st.s[j] = spp[j][k * (GK / kGroup)];
     };
-
-    RStage R0, R1, R2, R3;
+    RStage R0, R1;
     gload(0, R0);
     gload(1, R1);
-    gload(2, R2);
-    gload(3, R3);
 
     // ---- the requantised level table: thread tid fills code tid / 2, levels 8 (tid % 2) ..
     float cmax = 0.0f;
@@ -122,21 +131,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_rq(LinearArgs a, int tiles
     }
     __syncthreads();
 
-    int8_t *const xdst = &xs[0][xr * kPitch + 32 * xh];
-    int8_t *const wdst = &ws[0][wr * kPitch + 16 * wq];   // row wr; row wr + 128 is 128 rows on
-    auto decode16 = [&](uint32_t code, uint2 p) {
-        const uint4 tv = *reinterpret_cast<const uint4 *>(&tab[code * kLevels]);
+    auto tabrd = [&](uint32_t code) { return *reinterpret_cast<const uint4 *>(&tab[code * kLevels]); };
+    auto decode16 = [&](uint4 tv, uint2 p) {
         const CbI8 c{{tv.x, tv.y, tv.z, tv.w}};
         const uint2 lo = decode8(c, p.x), hi = decode8(c, p.y);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     };
-    auto lstore = [&](auto bufc, const RStage &st) {
-        constexpr int buf = decltype(bufc)::value;
-        int4v *dx = reinterpret_cast<int4v *>(xdst + buf * kXSt);
-        dx[0] = st.x0;
-        dx[1] = st.x1;
-        *reinterpret_cast<uint4 *>(wdst + buf * kWSt) = decode16(st.s0, st.p0);
-        if (w1st) *reinterpret_cast<uint4 *>(wdst + buf * kWSt + 128 * kPitch) = decode16(st.s1, st.p1);
+    auto xstore = [&](int buf, const RStage &st) {
+#pragma unroll
+        for (int j = 0; j < XJ; j++)
+            *reinterpret_cast<int4v *>(&xs[buf * kXSt + (sr + 64 * j) * kPitch + 16 * sc]) = st.x[j];
+    };
+    auto wstore = [&](int buf, int j, uint4 v) {
+        *reinterpret_cast<uint4 *>(&ws[buf * kWSt + (sr + 64 * j) * kPitch + 16 * sc]) = v;
     };
 
     int16v acc[2][GJB];
@@ -145,47 +152,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_rq(LinearArgs a, int tiles
 #pragma unroll
         for (int j = 0; j < GJB; j++) acc[i][j] = int16v{};
 
-    lstore(RIC<0>{}, R0);
+    xstore(0, R0);
+#pragma unroll
+    for (int j = 0; j < WJ; j++) wstore(0, j, decode16(tabrd(R0.s[j]), R0.p[j]));
     __syncthreads();
 
     const int half = lane >> 5, l32 = lane & 31;
-    const int8_t *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 16 * half];
-    const int8_t *const wrd = &ws[0][(wn * (GN / 2) + l32) * kPitch + 16 * half];
-    auto mfmas = [&](auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
+    const int8_t *const xrd = &xs[(wm * 64 + l32) * kPitch + 16 * half];
+    const int8_t *const wrd = &ws[(wn * (GN / 2) + l32) * kPitch + 16 * half];
+    // A and B lanes carry the same 16 k of a 32-wide step, so the product is the full sum
+    // over the step whatever order the unit takes them in
+    auto frag = [&](int buf, int s, Frag &f) {
 #pragma unroll
-        for (int s = 0; s < GK / 32; s++) {
-            int4v A[2], B[GJB];
+        for (int ib = 0; ib < 2; ib++)
+            f.A[ib] = *reinterpret_cast<const int4v *>(xrd + buf * kXSt + ib * 32 * kPitch + s * 32);
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++)
-                A[ib] = *reinterpret_cast<const int4v *>(xrd + buf * kXSt + ib * 32 * kPitch + s * 32);
-#pragma unroll
-            for (int jb = 0; jb < GJB; jb++)
-                B[jb] = *reinterpret_cast<const int4v *>(wrd + buf * kWSt + jb * 32 * kPitch + s * 32);
-            // A and B lanes carry the same 16 k of the 32-wide step, so the product is the
-            // full sum over the step whatever order the unit takes them in
-#pragma unroll
-            for (int ib = 0; ib < 2; ib++)
-#pragma unroll
-                for (int jb = 0; jb < GJB; jb++)
-                    acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
-        }
+        for (int jb = 0; jb < GJB; jb++)
+            f.B[jb] = *reinterpret_cast<const int4v *>(wrd + buf * kWSt + jb * 32 * kPitch + s * 32);
     };
-    // step s (ring slot J = s % 4): its stage is in LDS buffer J % 2; the slot reloads stage
-    // s + 4; stage s + 1 (loaded three steps ago) is decoded into the other buffer
-    auto step = [&](int s, auto jc, RStage &Rcur, RStage &Rnext) {
-        constexpr int J = decltype(jc)::value;
-        gload(s + 4, Rcur);
-        lstore(RIC<(J + 1) % 2>{}, Rnext);
-        mfmas(RIC<J % 2>{});
+    auto mma3 = [&](const Frag &f, int ib) {
+#pragma unroll
+        for (int jb = 0; jb < GJB; jb++)
+            acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.A[ib], f.B[jb], acc[ib][jb], 0, 0, 0);
+    };
+    // One stage: the MFMAs of buffer cur (four 32-k steps) while stage data nx is staged
+    // into buffer cur ^ 1.  The scheduling barriers keep this issue order: the fragments of
+    // step t + 1 and the table read of the next group go out before step t's MFMAs, and a
+    // group's lookups sit between two halves of a step's MFMAs.
+    auto stage = [&](auto curc, const RStage &nx) {
+        constexpr int cur = decltype(curc)::value, oth = cur ^ 1;
+        Frag F0, F1;
+        frag(cur, 0, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        uint4 tv = tabrd(nx.s[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        xstore(oth, nx);
+        frag(cur, 1, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma3(F0, 0);
+        const uint4 d0 = decode16(tv, nx.p[0]);
+        mma3(F0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 0, d0);
+        tv = tabrd(nx.s[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        frag(cur, 2, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma3(F1, 0);
+        const uint4 d1 = decode16(tv, nx.p[1]);
+        mma3(F1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 1, d1);
+        tv = tabrd(nx.s[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        frag(cur, 3, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma3(F0, 0);
+        const uint4 d2 = decode16(tv, nx.p[2]);
+        mma3(F0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 2, d2);
+        __builtin_amdgcn_sched_barrier(0);
+        mma3(F1, 0);
+        mma3(F1, 1);
+    };
+    // stage s is in LDS buffer s % 2 and stage s + 1 in ring slot (s + 1) % 2; the slot of
+    // stage s (already staged) is reloaded with stage s + 2 first
+    for (int s = 0; s < nk; s += 2) {
+        gload(s + 2, R0);
+        stage(RIC<0>{}, R1);
         __syncthreads();
-    };
-    // nk = K / 64 is a multiple of 4 (K is a multiple of 256): whole ring turns only
-    for (int s = 0; s < nk; s += 4) {
-        step(s, RIC<0>{}, R0, R1);
-        step(s + 1, RIC<1>{}, R1, R2);
-        step(s + 2, RIC<2>{}, R2, R3);
-        step(s + 3, RIC<3>{}, R3, R0);
+        gload(s + 3, R1);
+        stage(RIC<1>{}, R0);
+        __syncthreads();
     }
 
     // lane holds weight row j = l32 of each 32 x 32 block and tokens 8(v/4) + 4 half + v%4

@@ -20,11 +20,15 @@
 // the row's int32 accumulator in LDS (integer adds: the result does not depend on order).
 //
 // Kernel W2 (prefill): int8 MFMA GEMM, v_mfma_i32_32x32x32_i8, 256 tokens x 192 rows per
-// 512-thread workgroup (4 x 2 waves of 64 x 96), one workgroup per CU, 64-byte K stages
-// double-buffered through LDS with the global loads four stages ahead in a ring of register
-// stages, int32 accumulation over all of K, scales applied once in the epilogue.  Tiles are
-// numbered so that each XCD works through a contiguous run of them, token tiles fastest,
-// which keeps a weight tile's reuse within one XCD's L2.
+// 512-thread workgroup (4 x 2 waves of 64 x 96), one workgroup per CU, int32 accumulation
+// over all of K, scales applied once in the epilogue.  The skeleton is the W4A8 prefill
+// kernel's on requantised weights, so that the two compare like for like: 128-byte K
+// stages double-buffered through LDS in 144-byte rows, global loads of whole 128-byte lines
+// (eight lanes per row, eight rows per load) one stage ahead in a ring of two register
+// stages, and a hand-scheduled stage in which the fragments of 32-k step t + 1 are read,
+// and the next stage's rows stored, while step t's MFMAs run.  Tiles are numbered so that
+// each XCD works through a contiguous run of them, token tiles fastest, which keeps a
+// weight tile's reuse within one XCD's L2.
 #include <type_traits>
 
 #include "w4a8_internal.h"
@@ -156,26 +160,31 @@ __global__ __launch_bounds__(kGvThreads) void k_w8_gemv(W8Args a) {
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int16v __attribute__((ext_vector_type(16)));
 
-constexpr int GM = 256, GN = 192, GK = 64;  // tile: tokens x weight rows x K bytes per stage
+constexpr int GM = 256, GN = 192, GK = 128;  // tile: tokens x weight rows x K bytes per stage
 constexpr int kGmThreads = 512;
 constexpr int GJB = GN / 64;                // 32-row weight blocks per wave
-// 80-byte LDS rows: the 16 rows one 16-lane phase of a 16-byte fragment read touches start
-// at distinct multiples of 16 bytes modulo 256, i.e. on disjoint bank quads of the 64 banks
+// 144-byte LDS rows: the 16 rows one 16-lane phase of a 16-byte fragment read touches start
+// on distinct bank quads of the 64 banks
 constexpr int kPitch = GK + 16;
 constexpr int kXSt = GM * kPitch, kWSt = GN * kPitch;
+constexpr int XJ = GM / 64, WJ = GN / 64;   // staged rows per thread: 4 activation, 3 weight
 
 struct GStage {
-    int4v x0, x1;   // 32 activation bytes of token xr
-    int4v w0, w1;   // 16 weight bytes of rows wr and wr + 128 (the latter for threads < 256)
+    int4v x[XJ];   // 16 activation bytes of rows sr + 64 j
+    int4v w[WJ];   // 16 weight bytes of rows sr + 64 j
+};
+
+struct GFrag {
+    int4v A[2], B[GJB];
 };
 
 template <int J>
 using GIC = std::integral_constant<int, J>;
 
-// two waves per SIMD: the accumulators and the register ring need up to 256 registers
+// two waves per SIMD: the accumulators, two fragment sets and the register ring
 __global__ __launch_bounds__(kGmThreads, 1) void k_w8_gemm(W8Args a, int tiles_m, int tiles) {
-    __shared__ __align__(16) int8_t xs[2][kXSt];
-    __shared__ __align__(16) int8_t ws[2][kWSt];
+    __shared__ __align__(16) int8_t xs[2 * kXSt];
+    __shared__ __align__(16) int8_t ws[2 * kWSt];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -187,37 +196,33 @@ __global__ __launch_bounds__(kGmThreads, 1) void k_w8_gemm(W8Args a, int tiles_m
     const int t = xcd * q + min(xcd, rem) + slot;
     const int64_t m0 = (int64_t)(t % tiles_m) * GM, n0 = (int64_t)(t / tiles_m) * GN;
 
-    // staging: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight rows wr and wr + 128,
-    // bytes [16 wq, 16 wq + 16) (rows 128 .. 191 by threads < 256).  Rows past M or N re-read
-    // the last valid row: they feed only outputs that are never stored.  Threads past 256
-    // load a second row like row 191's but store nothing.
-    static_assert(GN > 128 && GN <= 256 && kGmThreads == 512, "weight staging covers 128 + (GN - 128) rows");
-    const int xr = tid >> 1, xh = tid & 1;
-    const int wr = tid >> 2, wq = tid & 3;
-    const bool w1st = wr < GN - 128;               // wave-uniform: 4 (GN - 128) is a multiple of 64
-    const int8_t *xp = a.x_q + min<int64_t>(m0 + xr, M - 1) * K + 32 * xh;
-    const int8_t *wp0 = a.w_q + min<int64_t>(n0 + wr, N - 1) * K + 16 * wq;
-    const int8_t *wp1 = a.w_q + min<int64_t>(n0 + (w1st ? 128 + wr : GN - 1), N - 1) * K + 16 * wq;
-    const int nk = (int)(K / GK);
+    // staging: rows sr + 64 j, 16-byte chunk sc of the stage.  Rows past M or N re-read the
+    // last valid row: they feed only outputs that are never stored.
+    const int sr = tid >> 3, sc = tid & 7;
+    const int8_t *xp[XJ];
+    const int8_t *wp[WJ];
+#pragma unroll
+    for (int j = 0; j < XJ; j++) xp[j] = a.x_q + min<int64_t>(m0 + sr + 64 * j, M - 1) * K + 16 * sc;
+#pragma unroll
+    for (int j = 0; j < WJ; j++) wp[j] = a.w_q + min<int64_t>(n0 + sr + 64 * j, N - 1) * K + 16 * sc;
+    const int nk = (int)(K / GK);  // even: K is a multiple of 256
 
     // every stage's loads are issued unconditionally (stages past the end re-read the last
     // one) so that the in-order load counter lets a store wait for its own stage only
     auto gload = [&](int kt, GStage &st) {
         const int64_t k = (int64_t)(kt < nk ? kt : nk - 1) * GK;
-        st.x0 = *reinterpret_cast<const int4v *>(xp + k);
-        st.x1 = *reinterpret_cast<const int4v *>(xp + k + 16);
-        st.w0 = *reinterpret_cast<const int4v *>(wp0 + k);
-        st.w1 = *reinterpret_cast<const int4v *>(wp1 + k);
+#pragma unroll
+        for (int j = 0; j < XJ; j++) st.x[j] = *reinterpret_cast<const int4v *>(xp[j] + k);
+#pragma unroll
+        for (int j = 0; j < WJ; j++) st.w[j] = *reinterpret_cast<const int4v *>(wp[j] + k);
     };
-    int8_t *const xdst = &xs[0][xr * kPitch + 32 * xh];
-    int8_t *const wdst = &ws[0][wr * kPitch + 16 * wq];   // row wr; row wr + 128 is 128 rows on
-    auto lstore = [&](auto bufc, const GStage &st) {
-        constexpr int buf = decltype(bufc)::value;
-        int4v *dx = reinterpret_cast<int4v *>(xdst + buf * kXSt);
-        dx[0] = st.x0;
-        dx[1] = st.x1;
-        *reinterpret_cast<int4v *>(wdst + buf * kWSt) = st.w0;
-        if (w1st) *reinterpret_cast<int4v *>(wdst + buf * kWSt + 128 * kPitch) = st.w1;
+    auto xstore = [&](int buf, const GStage &st) {
+#pragma unroll
+        for (int j = 0; j < XJ; j++)
+            *reinterpret_cast<int4v *>(&xs[buf * kXSt + (sr + 64 * j) * kPitch + 16 * sc]) = st.x[j];
+    };
+    auto wstore = [&](int buf, int j, const GStage &st) {
+        *reinterpret_cast<int4v *>(&ws[buf * kWSt + (sr + 64 * j) * kPitch + 16 * sc]) = st.w[j];
     };
 
     int16v acc[2][GJB];
@@ -226,52 +231,70 @@ __global__ __launch_bounds__(kGmThreads, 1) void k_w8_gemm(W8Args a, int tiles_m
 #pragma unroll
         for (int j = 0; j < GJB; j++) acc[i][j] = int16v{};
 
-    GStage R0, R1, R2, R3;
+    GStage R0, R1;
     gload(0, R0);
     gload(1, R1);
-    gload(2, R2);
-    gload(3, R3);
-    lstore(GIC<0>{}, R0);
+    xstore(0, R0);
+#pragma unroll
+    for (int j = 0; j < WJ; j++) wstore(0, j, R0);
     __syncthreads();
 
     const int half = lane >> 5, l32 = lane & 31;
-    const int8_t *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 16 * half];
-    const int8_t *const wrd = &ws[0][(wn * (GN / 2) + l32) * kPitch + 16 * half];
-    auto mfmas = [&](auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
+    const int8_t *const xrd = &xs[(wm * 64 + l32) * kPitch + 16 * half];
+    const int8_t *const wrd = &ws[(wn * (GN / 2) + l32) * kPitch + 16 * half];
+    // A and B lanes carry the same 16 k of a 32-wide step, so the product is the full sum
+    // over the step whatever order the unit takes them in
+    auto frag = [&](int buf, int s, GFrag &f) {
 #pragma unroll
-        for (int s = 0; s < GK / 32; s++) {
-            int4v A[2], B[GJB];
+        for (int ib = 0; ib < 2; ib++)
+            f.A[ib] = *reinterpret_cast<const int4v *>(xrd + buf * kXSt + ib * 32 * kPitch + s * 32);
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++)
-                A[ib] = *reinterpret_cast<const int4v *>(xrd + buf * kXSt + ib * 32 * kPitch + s * 32);
+        for (int jb = 0; jb < GJB; jb++)
+            f.B[jb] = *reinterpret_cast<const int4v *>(wrd + buf * kWSt + jb * 32 * kPitch + s * 32);
+    };
+    auto mma = [&](const GFrag &f) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++)
 #pragma unroll
             for (int jb = 0; jb < GJB; jb++)
-                B[jb] = *reinterpret_cast<const int4v *>(wrd + buf * kWSt + jb * 32 * kPitch + s * 32);
-            // A and B lanes carry the same 16 k of the 32-wide step, so the product is the
-            // full sum over the step whatever order the unit takes them in
-#pragma unroll
-            for (int ib = 0; ib < 2; ib++)
-#pragma unroll
-                for (int jb = 0; jb < GJB; jb++)
-                    acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
-        }
+                acc[ib][jb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.A[ib], f.B[jb], acc[ib][jb], 0, 0, 0);
     };
-    // step s (ring slot J = s % 4): its stage is in LDS buffer J % 2; the slot reloads stage
-    // s + 4; stage s + 1 (loaded three steps ago) is staged into the other buffer
-    auto step = [&](int s, auto jc, GStage &Rcur, GStage &Rnext) {
-        constexpr int J = decltype(jc)::value;
-        gload(s + 4, Rcur);
-        lstore(GIC<(J + 1) % 2>{}, Rnext);
-        mfmas(GIC<J % 2>{});
+    // One stage: the MFMAs of buffer cur (four 32-k steps) while stage data nx is stored
+    // into buffer cur ^ 1.  The scheduling barriers keep the fragments of step t + 1 (and a
+    // share of the stores) ahead of step t's MFMAs.
+    auto stage = [&](auto curc, const GStage &nx) {
+        constexpr int cur = decltype(curc)::value, oth = cur ^ 1;
+        GFrag F0, F1;
+        frag(cur, 0, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        xstore(oth, nx);
+        frag(cur, 1, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F0);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 0, nx);
+        frag(cur, 2, F0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F1);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 1, nx);
+        frag(cur, 3, F1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F0);
+        __builtin_amdgcn_sched_barrier(0);
+        wstore(oth, 2, nx);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(F1);
+    };
+    // stage s is in LDS buffer s % 2 and stage s + 1 in ring slot (s + 1) % 2; the slot of
+    // stage s (already stored) is reloaded with stage s + 2 first
+    for (int s = 0; s < nk; s += 2) {
+        gload(s + 2, R0);
+        stage(GIC<0>{}, R1);
         __syncthreads();
-    };
-    // nk = K / 64 is a multiple of 4 (K is a multiple of 256): whole ring turns only
-    for (int s = 0; s < nk; s += 4) {
-        step(s, GIC<0>{}, R0, R1);
-        step(s + 1, GIC<1>{}, R1, R2);
-        step(s + 2, GIC<2>{}, R2, R3);
-        step(s + 3, GIC<3>{}, R3, R0);
+        gload(s + 3, R1);
+        stage(GIC<1>{}, R0);
+        __syncthreads();
     }
 
     // lane holds weight row j = l32 of each 32 x 32 block and tokens 8(v/4) + 4 half + v%4
