@@ -556,7 +556,8 @@ def w8a8_model(w, torch, S, tokens=10):
 def pmc_pass(w, torch, S, shapes):
     """Eager launches for the counter runs: a plain elementwise copy of CALIB_BYTES (reads and
     writes that many bytes once) for calibration, then the MLP block's fused launches (gate+up,
-    down) and the prepared-input GEMV on every weight copy, then the two prefill GEMMs."""
+    down) and the prepared-input GEMV on every weight copy, then the prefill GEMMs (three W4A8 routes
+    and the W8A8 comparator) on both MLP shapes."""
     a = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -584,6 +585,9 @@ def pmc_pass(w, torch, S, shapes):
         y = torch.empty((2048, n), dtype=torch.float32, device="cuda")
         for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ):
             w.linear(xq, sx, L, out=y, algo=algo)
+        W8 = w.w8a8_quantize_weight(torch.from_numpy(S.weights(n, k, seed=0)).cuda())
+        w.w8a8_linear(xq, sx, W8, out=y, algo=w.ALGO_MFMA_I8)
+        del W8
     torch.cuda.synchronize()
     log("pmc pass done")
 
