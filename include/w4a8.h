@@ -64,8 +64,7 @@ typedef enum { W4A8_F32 = 0, W4A8_BF16 = 1 } w4a8_dtype;
 /* Kernel choice for w4a8_linear_algo. */
 typedef enum {
     W4A8_ALGO_AUTO = 0,       /* pick by M, N, K (what w4a8_linear does): GEMV within its
-                                 range (at M = 4 only for N < 8192), SKINNY for M <= 64,
-                                 else MFMA_F16 */
+                                 range for M <= 3, SKINNY for M <= 64, else MFMA_F16 */
     W4A8_ALGO_GEMV = 1,       /* fp32-codebook streaming GEMV (decode); M <= 4 and M*K <= 40960 */
     W4A8_ALGO_MFMA_I8 = 2,    /* int8 MFMA on the int8 form of the codebook, exact int32
                                  per-16 partials, fp32 group-scale fold */

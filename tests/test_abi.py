@@ -54,7 +54,7 @@ def test_workspace_size_and_pick(L):
     assert L.w4a8_linear_pick(1, 17408, 5120) == w.ALGO_GEMV
     assert L.w4a8_linear_pick(2, 5120, 17408) == w.ALGO_GEMV
     assert L.w4a8_linear_pick(4, 17408, 5120) == w.ALGO_MFMA_SKINNY
-    assert L.w4a8_linear_pick(4, 5120, 5120) == w.ALGO_GEMV
+    assert L.w4a8_linear_pick(4, 5120, 5120) == w.ALGO_MFMA_SKINNY
     assert L.w4a8_linear_pick(3, 17408, 5120) == w.ALGO_GEMV
     assert L.w4a8_linear_pick(3, 5120, 17408) == w.ALGO_MFMA_SKINNY
     assert L.w4a8_linear_pick(5, 17408, 5120) == w.ALGO_MFMA_SKINNY

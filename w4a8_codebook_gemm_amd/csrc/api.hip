@@ -50,9 +50,8 @@ int check_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, cons
 }
 
 int pick(int64_t M, int64_t N, int64_t K) {
-    // the GEMV up to M = 3; at M = 4 the skinny kernel is as fast or faster once the rows
-    // fill the chip several times over (measured crossover)
-    if (w4a8::gemv_supported(M, K) && (M < 4 || N < 8192)) return W4A8_ALGO_GEMV;
+    // the GEMV up to M = 3; from M = 4 the skinny kernel is faster (measured crossover)
+    if (w4a8::gemv_supported(M, K) && M <= 3) return W4A8_ALGO_GEMV;
     if (w4a8::skinny_supported(M, N, K)) return W4A8_ALGO_MFMA_SKINNY;
     return W4A8_ALGO_MFMA_F16;
 }

@@ -23,10 +23,11 @@
 //    Tokens past M and rows past N read zero through the buffer bounds.
 //  * A workgroup owns NT consecutive 16-row tiles; its waves (4 to 16, as registers allow)
 //    split K (wave w takes every W-th 128-k half-block, so the waves stream adjacent pieces
-//    of the same rows together) and each keeps its NT x MT16 accumulator tiles in registers.  Every
-//    half-block's loads are issued two half-blocks ahead (a ring of three).  At the end the
-//    waves' partial tiles are summed through LDS in wave order (deterministic) and scaled
-//    by 2^(ex-8) s_ch s_x.
+//    of the same rows together) and each keeps its NT x MT16 accumulator tiles in registers.
+//    Each wave's next half-block is in flight while it computes one (a ring of two; a third
+//    half-block in flight was 4-11% slower at M = 8 and 32).  At the end the waves' partial
+//    tiles are summed through LDS in wave order (deterministic) and scaled by
+//    2^(ex-8) s_ch s_x.
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
 //  * Start-up: the codebook and the workgroup's group scales are requested before the first
 //    weight loads (a request behind them waits for them to drain from HBM); the scales go
@@ -139,10 +140,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
         }
     };
 
-    Slot<NT, MT16> R0, R1, R2;
+    Slot<NT, MT16> R0, R1;
     fetch(h0, R0);
     fetch(h0 + S, R1);
-    fetch(h0 + 2 * S, R2);
 
     // codebook -> fp16 pair table scaled by 2^-ex; wave w writes 16 / WAVES high nibbles
     float cmax = 0.0f;
@@ -165,10 +165,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
             tab[(16 * hi_n + lo) * 64 + lane] = v;
         }
     }
-    // every copy to LDS of this wave is complete once at most the three ring stages' loads
+    // every copy to LDS of this wave is complete once at most the two ring stages' loads
     // (issued after them) are outstanding (gfx9 s_waitcnt encoding: vmcnt in bits 3..0 and
     // 15..14, no expcnt / lgkmcnt wait); the barrier then publishes them
-    constexpr int kRingLoads = 3 * (NT + 2 * MT16);
+    constexpr int kRingLoads = 2 * (NT + 2 * MT16);
     static_assert(kRingLoads < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kRingLoads & 15) | ((kRingLoads >> 4) << 14));
     __syncthreads();
@@ -222,13 +222,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
 
     // Fetches are unconditional (half-blocks past the range read zero) so the number of
     // loads in flight is the same on every path and each compute waits only for its own.
-    for (int h = h0; h < h1; h += 3 * S) {
+    for (int h = h0; h < h1; h += 2 * S) {
         compute(h, R0);
-        fetch(h + 3 * S, R0);
+        fetch(h + 2 * S, R0);
         if (h + S < h1) compute(h + S, R1);
-        fetch(h + 4 * S, R1);
-        if (h + 2 * S < h1) compute(h + 2 * S, R2);
-        fetch(h + 5 * S, R2);
+        fetch(h + 3 * S, R1);
     }
     // Wave partials are summed through LDS one token tile at a time, in wave order
     // (deterministic): [wave][t][lane] float4, lane holding rows 4 lq .. 4 lq + 3 of the
