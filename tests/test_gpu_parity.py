@@ -321,6 +321,33 @@ def test_mfma_rq_every_scale_code(w):
     assert np.array_equal(y.view(np.uint32), yq.view(np.uint32))
 
 
+def test_mfma_rq_longest_rows_extreme_values(w):
+    """K = 131072, the longest rows the route takes, with every product at +-127 x 127: the
+    int32 sums reach 127^2 K = 2.11e9, just under 2^31, and must stay exact.  Rows alternate
+    the sign of their level; sampled rows and tokens against the oracle, bit for bit."""
+    N, K, M = 200, 131072, 300
+    say(f"mfma_rq extreme N={N} K={K} M={M}")
+    cb = np.linspace(-1.0, 1.0, 16).astype(np.float32)        # levels 0 and 15 map to -127 / +127
+    packed = np.full((N, K // 2), -1, dtype=np.int8)           # index 15 in both nibbles
+    packed[1::2] = 0                                           # index 0
+    s_rel = np.full((N, K // 16), 0x38, dtype=np.uint8)        # 1.0
+    s_ch = np.full(N, 0.5, dtype=np.float32)
+    xq = np.full((M, K), 127, dtype=np.int8)
+    xq[::3] = -127
+    sx = np.full(M, 0.25, dtype=np.float32)
+    L = w.QuantizedLinear(gpu(packed), gpu(s_rel), gpu(s_ch), gpu(cb))
+    y = w.linear(gpu(xq), gpu(sx), L, algo=w.ALGO_MFMA_RQ)
+    torch.cuda.synchronize()
+    rows, toks = sample(N, 24, 3), sample(M, 24, 4)
+    y = y.cpu().numpy()[np.ix_(toks, rows)]
+    yq = O.linear_rq_ref(xq, sx, packed, s_rel, s_ch, cb, rows, toks)
+    assert np.array_equal(y.view(np.uint32), yq.view(np.uint32))
+    t = O.rq_table(cb)
+    assert t[0x38, 15] == 127 and t[0x38, 0] == -127
+    sw = np.float32(0.5) * (np.float32(1.0) / np.float32(127.0))   # s_channel * s_cb
+    assert np.abs(yq).max() == (np.float32(127 * 127 * K) * sw) * np.float32(0.25)
+
+
 def test_mfma_rq_bf16_output(w):
     N, K, M = 385, 768, 300
     say(f"mfma_rq bf16 N={N} K={K} M={M}")
