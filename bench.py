@@ -56,6 +56,18 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
+FP32_VALU_LANE_OPS = 78.65e12   # fp32 vector peak 157.3 TFLOP/s counts an FMA as two
+
+
+def fold_ceiling_tops():
+    """What the exact per-16 fold allows: every int32 group partial (M N K / 16 of them) takes
+    a conversion and an fma on the vector ALU (two lane operations), and the MFMA that covers
+    one group of 16 (v_mfma_i32_32x32x16_i8) runs at half the int8 peak.  Issued one after the
+    other the two take 2 M N K / (T_valu + T_mfma) with T_valu = (M N K / 8) / FP32_VALU_LANE_OPS
+    and T_mfma = 2 M N K / (peak / 2); the ratio does not depend on M, N or K."""
+    t_valu = (1.0 / 8.0) / FP32_VALU_LANE_OPS          # per multiply-accumulate
+    t_mfma = 2.0 / (INT8_PEAK_TOPS * 1e12 / 2.0)
+    return 2.0 / (t_valu + t_mfma) / 1e12
 COPIES = 8
 METRIC = "W4A8 linear: effective weight GB/s (M=1) + int8 TOPS (M=2048) on 1 MI355X"
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
@@ -419,6 +431,8 @@ def prefill(w, torch, S, shapes, M=2048):
         mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
         summary[name] = dict(tops=round(mean, 1), roofline=dict(
             bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
+    fc = fold_ceiling_tops()
+    summary["mfma_i8"]["fold_ceiling"] = dict(tops=round(fc, 1), frac=round(summary["mfma_i8"]["tops"] / fc, 4))
     del pl
     return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
 
