@@ -41,6 +41,7 @@ calibration) and prints nothing else: it is the program profiled by the counter 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -147,6 +148,37 @@ def make_graph(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def read_ceiling(torch, nbytes, copies=COPIES):
+    """The achievable HBM read rate at nbytes per launch: a plain streaming read (the helper
+    kernel of bench_read.hip) over `copies` distinct buffers, as the decode kernels rotate
+    through weight copies; the best of three grid sizes.  None when the helper is not built."""
+    path = os.path.join(ROOT, "bench_read.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.bench_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.bench_read_launch.restype = ctypes.c_int
+    n = nbytes // 16 * 16
+    bufs = [torch.full((n,), c + 1, dtype=torch.uint8, device="cuda") for c in range(copies)]
+    best = 0.0
+    for blocks in (256, 512, 1024):
+        sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+
+        def launch():
+            st = torch.cuda.current_stream().cuda_stream
+            for b in bufs:
+                rc = lib.bench_read_launch(b.data_ptr(), n, sink.data_ptr(), blocks, st)
+                if rc != 0:
+                    raise RuntimeError(f"bench_read_launch: HIP error {rc}")
+        g = make_graph(torch, launch)
+        t = time_graph(torch, g, 20) / copies
+        best = max(best, n / t / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
 
 
 def busy(torch):
@@ -280,6 +312,12 @@ def decode(w, torch, S, args, shapes):
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="k_gemv<1,1,8> (fused rotate + quantise + W4A8 GEMV of gate and up, fp32 x)",
                     per_launch_bytes=int(per_gu), avg_launch_us=round(t_gu * 1e6, 3))
+    rc = read_ceiling(torch, int(per_gu))
+    if rc:
+        roofline["read_ceiling_gbs"] = round(rc, 1)
+        roofline["frac_of_read_ceiling"] = round(ach / rc, 4)
+        log(f"plain read of {per_gu / 1e6:.1f} MB per launch: {rc:.1f} GB/s; the fused gate+up launch "
+            f"reaches {ach / rc * 100:.1f}% of it")
     down_k = dict(kernel="k_gemv<1,1,1> (fused rotate + quantise + W4A8 GEMV of down, fp32 x)",
                   avg_launch_us=round(t_dn * 1e6, 3), per_launch_bytes=int(per_dn),
                   achieved=round(per_dn / t_dn / 1e9, 1), frac=round(per_dn / t_dn / 1e9 / HBM_PEAK_GBS, 4))
