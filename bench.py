@@ -219,9 +219,20 @@ def cpu_baseline(shapes, target_s=10.0):
         if el >= target_s:
             break
     byt = sum(weight_bytes(n, k) for (n, k, _, _) in prep) * reps
+    # prefill beside it: the fp64 product of 256 rows x 2048 tokens of the gate/up shape (a
+    # slice of the M = 2048 GEMM, whose cost scales linearly with the rows)
+    n, k, q, _ = prep[0]
+    xq, sx = O.prepare(S.activations(2048, k, seed=0))
+    rows = np.arange(256)
+    t1 = time.perf_counter()
+    O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, None)
+    tp = time.perf_counter() - t1
     return dict(value=round(byt / el / 1e9, 3), unit="GB/s", cores=O.num_threads(), kind="oracle",
                 sample=f"{reps} full M=1 passes (prepare + fp64 product over all rows) of both "
-                       f"shapes 17408x5120 and 5120x17408, {el:.1f} s")
+                       f"shapes 17408x5120 and 5120x17408, {el:.1f} s",
+                prefill_gops=round(2.0 * 2048 * 256 * k / tp / 1e9, 2),
+                prefill_sample=f"fp64 product of 256 of the {n} rows x 2048 tokens at K = {k}, {tp:.2f} s "
+                               f"(the full GEMM would take {tp * n / 256:.0f} s)")
 
 
 def mlp_layers(w, torch, S, copies):
