@@ -29,6 +29,8 @@
 //    tiles are summed through LDS in wave order (deterministic) and scaled by
 //    2^(ex-8) s_ch s_x.
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
+//    Up to 48 tokens the table reads of the next row tile are issued before the current
+//    tile's multiplies and MFMAs (scheduling barriers keep that order).
 //  * Start-up: the codebook and the workgroup's group scales are requested before the first
 //    weight loads (a request behind them waits for them to drain from HBM); the scales go
 //    straight to LDS through the buffer unit (16 B per lane), so the weight stream carries
@@ -193,6 +195,43 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
             for (int st = 0; st < 4; st++)
                 B[u][st] = __builtin_bit_cast(half8_t, make_uint4(f[4 * st], f[4 * st + 1], f[4 * st + 2], f[4 * st + 3]));
         }
+        if constexpr (MT16 <= 3) {
+            // the table reads (and the scale read) of tile t + 1 go out before tile t's
+            // multiplies and MFMAs, so that their LDS latency is not paid tile by tile (kept
+            // off at four token tiles, where the extra registers cost more than it saves)
+            uint32_t pr[2][16], srr[2];
+            auto reads = [&](int t, uint32_t (&p)[16], uint32_t &sr) {
+                sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grpbytes + 8u * (uint32_t)h + 2u * lq);
+                const uint32_t pw[4] = {s.pk[t].x, s.pk[t].y, s.pk[t].z, s.pk[t].w};
+#pragma unroll
+                for (int st = 0; st < 4; st++)
+#pragma unroll
+                    for (int c = 0; c < 4; c++)
+                        p[4 * st + c] = *reinterpret_cast<const uint32_t *>(
+                            smem + __builtin_amdgcn_perm(lanebase, pw[st], 0x0C0C0004u | ((uint32_t)c << 8)));
+            };
+            reads(0, pr[0], srr[0]);
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                if (t + 1 < NT) reads(t + 1, pr[(t + 1) & 1], srr[(t + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t sr = srr[t & 1];
+                const uint32_t s0 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 0) * 256.0f));
+                const uint32_t s1 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 1) * 256.0f));
+                const uint32_t sg[2] = {s0 | (s0 << 16), s1 | (s1 << 16)};
+#pragma unroll
+                for (int st = 0; st < 4; st++) {
+                    uint32_t aw[4];
+#pragma unroll
+                    for (int c = 0; c < 4; c++) aw[c] = pk_mul(pr[t & 1][4 * st + c], sg[st >> 1]);
+                    const half8_t A = __builtin_bit_cast(half8_t, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+#pragma unroll
+                    for (int u = 0; u < MT16; u++)
+                        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[u][st], acc[t][u], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             // group scales of this lane's 32 values (row 16 t + li, groups 8 h + 2 lq and the
@@ -217,6 +256,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
                 for (int u = 0; u < MT16; u++)
                     acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[u][st], acc[t][u], 0, 0, 0);
             }
+        }
         }
     };
 
