@@ -174,7 +174,7 @@ def read_ceiling(torch, nbytes, copies=COPIES):
                 if rc != 0:
                     raise RuntimeError(f"bench_read_launch: HIP error {rc}")
         g = make_graph(torch, launch)
-        t = time_graph(torch, g, 20) / copies
+        t = time_kernel_graph(torch, g) / copies
         best = max(best, n / t / 1e9)
     del bufs
     torch.cuda.empty_cache()
@@ -185,6 +185,16 @@ def busy(torch):
     """Keep the GPU busy while the host enqueues what follows (no host-paced gaps)."""
     if hasattr(torch.cuda, "_sleep"):
         torch.cuda._sleep(20_000_000)
+
+
+def time_kernel_graph(torch, graph, replays=4, bursts=5):
+    """Per-kernel figures: the median over `bursts` short runs of `replays` graph replays, each
+    after the busy-wait.  A memory-bound launch sustained for milliseconds slows down by up to
+    about 12% (the power draw of a full-bandwidth stream); the headline step and the model are
+    timed sustained, the per-kernel rooflines in short runs, which is what a kernel trace of
+    the same launches records."""
+    ts = sorted(time_graph(torch, graph, replays) for _ in range(bursts))
+    return ts[len(ts) // 2]
 
 
 def time_graph(torch, graph, replays):
@@ -312,9 +322,10 @@ def decode(w, torch, S, args, shapes):
     # graph of its own launches; the down launch beside it
     reps = max(4, args.steps // (4 * COPIES))
     g_gu = make_graph(torch, lambda: [gate_up(c) for c in range(COPIES)])
-    t_gu = time_graph(torch, g_gu, reps) / COPIES
+    t_gu = time_kernel_graph(torch, g_gu) / COPIES
+    t_gu_sustained = time_graph(torch, g_gu, reps) / COPIES
     g_dn = make_graph(torch, lambda: [down(c) for c in range(COPIES)])
-    t_dn = time_graph(torch, g_dn, reps) / COPIES
+    t_dn = time_kernel_graph(torch, g_dn) / COPIES
     per_gu = multi_forward_bytes(ng, kg, 2)
     per_dn = forward_bytes(nd, kd)
     ach = per_gu / t_gu / 1e9
@@ -322,7 +333,8 @@ def decode(w, torch, S, args, shapes):
     roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="k_gemv<1,1,8> (fused rotate + quantise + W4A8 GEMV of gate and up, fp32 x)",
-                    per_launch_bytes=int(per_gu), avg_launch_us=round(t_gu * 1e6, 3))
+                    per_launch_bytes=int(per_gu), avg_launch_us=round(t_gu * 1e6, 3),
+                    avg_launch_us_sustained=round(t_gu_sustained * 1e6, 3))
     rc = read_ceiling(torch, int(per_gu))
     if rc:
         roofline["read_ceiling_gbs"] = round(rc, 1)
@@ -346,7 +358,7 @@ def decode(w, torch, S, args, shapes):
     gemv_g = make_graph(torch, lambda: [(w.linear(*xq_in, blocks[c]["gate"], out=y_gu[0], algo=w.ALGO_GEMV),
                                          w.linear(*xq_hid, blocks[c]["down"], out=y_dn, algo=w.ALGO_GEMV))
                                         for c in range(COPIES)])
-    t_gemv = time_graph(torch, gemv_g, reps) / (COPIES * 2)
+    t_gemv = time_kernel_graph(torch, gemv_g) / (COPIES * 2)
     per_gemv = (gemv_bytes(ng, kg) + gemv_bytes(nd, kd)) / 2
     log(f"GEMV (prepared x_q): {t_gemv * 1e6:.2f} us per launch, {per_gemv / t_gemv / 1e9:.1f} GB/s")
     gemv = dict(kernel="k_gemv<1,0,1> (prepared int8 x, one layer)", avg_launch_us=round(t_gemv * 1e6, 3),
@@ -379,10 +391,10 @@ def sweep(w, torch, S):
                     if e.status != 2:
                         raise
                     continue
-                point[name] = round(time_graph(torch, g, 8) / COPIES * 1e6, 2)
+                point[name] = round(time_kernel_graph(torch, g) / COPIES * 1e6, 2)
             g = make_graph(torch, lambda: [w.forward(x, layers[(n, k)][c], out=y, x_q=xq, s_x=sx)
                                            for c in range(COPIES)])
-            t_auto = time_graph(torch, g, 8) / COPIES
+            t_auto = time_kernel_graph(torch, g) / COPIES
             best = min(point, key=point.get)
             tb = point[best] * 1e-6
             res[f"{n}x{k}/M={m}"] = dict(
@@ -529,7 +541,7 @@ def w8a8(w, torch, S, shapes, w4_gemv, w4_unfused_us, w4_prefill, M=2048):
     ys = {(n, k): torch.empty((1, n), dtype=torch.float32, device="cuda") for (n, k) in shapes}
     g = make_graph(torch, lambda: [w.w8a8_linear(*xqs[sh], layers[sh][c], out=ys[sh], algo=w.ALGO_GEMV)
                                    for c in range(COPIES) for sh in shapes])
-    t_gemv = time_graph(torch, g, 25) / (COPIES * len(shapes))
+    t_gemv = time_kernel_graph(torch, g) / (COPIES * len(shapes))
     per = sum(w8_gemv_bytes(n, k) for (n, k) in shapes) / len(shapes)
 
     def step(c):
