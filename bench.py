@@ -681,8 +681,8 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              "multi-GPU path (how the layer would shard is described with the design)", file=sys.stderr)
         sys.exit(2)
 
     import torch
