@@ -180,7 +180,11 @@ def prepare_activation(x: torch.Tensor, out=None):
 
 def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32,
            algo: int = ALGO_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
-    """y [M, N] = the quantised product of prepared activations with one layer."""
+    """y [M, N] = the quantised product of prepared activations with one layer.
+
+    algo: ALGO_AUTO (what w4a8_linear picks), ALGO_GEMV, ALGO_MFMA_SKINNY, ALGO_MFMA_F16,
+    ALGO_MFMA_I8 (exact per-16 fold) or ALGO_MFMA_RQ (weights requantised to int8: an
+    approximation of the product, see w4a8.h)."""
     m, k = x_q.shape
     n = layer.packed.shape[0]
     if (tuple(layer.packed.shape) != (n, k // 2) or tuple(layer.s_rel.shape) != (n, k // 16)
