@@ -197,8 +197,8 @@ typedef struct {
  * Several layers that read the same activations (the query/key/value projections of one
  * input, or gate and up) in one call [card "...w4a8-convrot-ComfyUI", section "Why this
  * exists": decode re-reads every weight for every token, so each launch's fixed cost is paid
- * once per layer per token].  For GEMV sizes (M <= 4 and M*K <= 40960) all layers run in ONE
- * launch, its workgroups split between the layers in proportion to their rows; otherwise
+ * once per layer per token].  Where w4a8_linear takes the GEMV (M <= 3 and M*K <= 40960)
+ * all layers run in ONE launch, its workgroups split between the layers in proportion to their rows; otherwise
  * each layer runs as w4a8_linear would.  Every y is bit-identical to what w4a8_linear gives
  * for that layer alone.
  *

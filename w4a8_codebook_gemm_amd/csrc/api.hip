@@ -49,9 +49,13 @@ int check_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, cons
     return W4A8_OK;
 }
 
+// Where w4a8_linear takes the GEMV: within its range up to M = 3; from M = 4 the skinny
+// kernel is faster (measured crossover).  The multi-layer call follows the same rule so that
+// its outputs stay bit-identical to single-layer calls.
+inline bool gemv_auto(int64_t M, int64_t K) { return w4a8::gemv_supported(M, K) && M <= 3; }
+
 int pick(int64_t M, int64_t N, int64_t K) {
-    // the GEMV up to M = 3; from M = 4 the skinny kernel is faster (measured crossover)
-    if (w4a8::gemv_supported(M, K) && M <= 3) return W4A8_ALGO_GEMV;
+    if (gemv_auto(M, K)) return W4A8_ALGO_GEMV;
     if (w4a8::skinny_supported(M, N, K)) return W4A8_ALGO_MFMA_SKINNY;
     return W4A8_ALGO_MFMA_F16;
 }
@@ -188,7 +192,7 @@ int w4a8_linear_multi(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     w4a8::LayerDesc d[w4a8::kMaxGroup];
     int st = check_multi(x_q, s_x, M, K, G, layers, y_dtype, d);
     if (st != W4A8_OK) return st;
-    if (!w4a8::gemv_supported(M, K)) {
+    if (!gemv_auto(M, K)) {
         for (int g = 0; g < G; g++) {
             st = w4a8_linear(x_q, s_x, M, K, d[g].packed, d[g].s_rel, d[g].s_ch, d[g].cb, d[g].N, d[g].y,
                              y_dtype, stream);
