@@ -135,6 +135,26 @@ def test_w8_gemm_parity(w, N, K, M):
     assert_close(*run(w, w.ALGO_MFMA_I8, N, K, M))
 
 
+def test_w8_gemm_longest_rows_extreme_values(w):
+    """K = 131072, the longest rows the format takes, with every product at +-127 x 127: the
+    int32 sums reach 127^2 K = 2.11e9, just under 2^31, and must stay exact."""
+    N, K, M = 200, 131072, 300
+    say(f"w8 gemm extreme N={N} K={K} M={M}")
+    wq = np.full((N, K), 127, dtype=np.int8)
+    wq[1::2] = -127
+    sw = np.full(N, 0.5, dtype=np.float32)
+    xq = np.full((M, K), 127, dtype=np.int8)
+    xq[::3] = -127
+    sx = np.full(M, 0.25, dtype=np.float32)
+    y = w.w8a8_linear(gpu(xq), gpu(sx), w.W8Linear(gpu(wq), gpu(sw)), algo=w.ALGO_MFMA_I8)
+    torch.cuda.synchronize()
+    rows, toks = sample(N, 24, 5), sample(M, 24, 6)
+    y = y.cpu().numpy().astype(np.float64)[np.ix_(toks, rows)]
+    yr = O.linear_w8_ref(xq[toks], sx[toks], wq[rows], sw[rows])
+    assert np.abs(yr).max() == 127 * 127 * K * 0.5 * 0.25
+    assert_close(y, yr)
+
+
 @pytest.mark.parametrize("N,K,M,algo", [(17408, 5120, 1, 1), (5120, 17408, 2, 1), (17408, 5120, 2048, 2),
                                         (5120, 17408, 2048, 2)])
 def test_w8_full_size_sampled(w, N, K, M, algo):
