@@ -265,6 +265,31 @@ def test_mfma_f16_full_size_sampled(w, N, K):
     assert_gate(y, yr, A)
 
 
+@pytest.mark.parametrize("algo", ["mfma_i8", "mfma_f16"])
+def test_prefill_longest_rows(w, algo):
+    """K = 131072 (512 rotation blocks, 8192 groups per row) through the two exact-bound
+    prefill kernels: random layer bytes in the format's ranges, sampled rows and tokens against
+    the oracle's product (and, for the int8 route, its int8-codebook reading)."""
+    N, K, M = 200, 131072, 300
+    a = {"mfma_i8": w.ALGO_MFMA_I8, "mfma_f16": w.ALGO_MFMA_F16}[algo]
+    say(f"{algo} longest rows N={N} K={K} M={M}")
+    g = np.random.default_rng(12)
+    packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
+    s_rel = g.integers(0x20, 0x39, size=(N, K // 16), dtype=np.uint8)
+    s_ch = (0.01 + 0.02 * g.random(N)).astype(np.float32)
+    cb = np.sort(g.standard_normal(16)).astype(np.float32)
+    _, xq, sx = oracle_acts(M, K, 13, 2)
+    L = w.QuantizedLinear(gpu(packed), gpu(s_rel), gpu(s_ch), gpu(cb))
+    y = w.linear(gpu(xq), gpu(sx), L, algo=a)
+    torch.cuda.synchronize()
+    rows, toks = sample(N, 24, 7), sample(M, 24, 8)
+    y = y.cpu().numpy().astype(np.float64)[np.ix_(toks, rows)]
+    yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb, rows, toks)
+    assert_gate(y, yr, A)
+    if algo == "mfma_i8":
+        i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, rows, toks)
+
+
 # Requantised int8 weights: the kernel and the oracle take the same integer decisions (the
 # table of rounded group-scaled levels, exact int32 sums) and the same three fp32 roundings,
 # so the outputs are compared bit for bit; the gate against the exact product is the
