@@ -311,7 +311,8 @@ def run_rq(w, N, K, M, rows=None, toks=None, out_dtype=torch.float32, seed=0, la
 
 
 @pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (512, 256, 257),
-                                   (17, 5120, 3), (385, 1280, 600), (193, 256, 65), (1000, 2048, 513)])
+                                   (17, 5120, 3), (385, 1280, 600), (193, 256, 65), (1000, 2048, 513),
+                                   (1, 256, 1)])
 def test_mfma_rq_parity(w, N, K, M):
     say(f"mfma_rq N={N} K={K} M={M}")
     y, yq, (xq, sx, layer) = run_rq(w, N, K, M)
