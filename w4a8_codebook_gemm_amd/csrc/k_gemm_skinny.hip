@@ -37,6 +37,7 @@
 //    no 2-byte loads.
 #include <type_traits>
 
+#include <atomic>
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -318,12 +319,13 @@ template <int NT, int MT16>
 hipError_t launch_one(const LinearArgs &a, unsigned grid, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
     const int64_t lds = kSmemBytes + skinny_scale_bytes(16 * NT, a.K / kGroup);
-    static bool attr_set = false;
-    if (!attr_set) {
+    // set once per kernel instance; concurrent first calls may both set it, which is harmless
+    static std::atomic<bool> attr_set{false};
+    if (!attr_set.load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_skinny<NT, MT16, W>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsMax);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a);
     return hipGetLastError();

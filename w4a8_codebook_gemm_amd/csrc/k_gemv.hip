@@ -37,6 +37,7 @@
 //  * Start-up: every small operand (codebook, row scales, activations) is requested before
 //    the first weight loads; a request issued behind them would wait for the whole first
 //    wave of weight traffic to drain from HBM before the table could be built.
+#include <atomic>
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -583,13 +584,14 @@ int64_t plan_rows(const LinearArgs &a, const LayerDesc *layers, int G, int num_c
 
 template <int MT, int XIN, int NG, bool SS>
 hipError_t launch_planned(const LinearArgs &a, const GroupTab<NG> &gt, int64_t lds, hipStream_t stream) {
-    static bool attr_set = false;
-    if (!attr_set) {
+    // set once per kernel instance; concurrent first calls may both set it, which is harmless
+    static std::atomic<bool> attr_set{false};
+    if (!attr_set.load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemv<MT, XIN, NG, SS>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kLdsMax - kTabWords * 4));
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL((k_gemv<MT, XIN, NG, SS>), dim3((unsigned)gt.wg_start[gt.G]), dim3(kThreads), (size_t)lds, stream, a, gt);
     return hipGetLastError();
