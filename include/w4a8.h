@@ -154,8 +154,9 @@ W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t
 /* As w4a8_linear with an explicit kernel choice (w4a8_algo).  W4A8_ALGO_GEMV returns
  * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960), W4A8_ALGO_MFMA_SKINNY outside
  * its range (M <= 64, M*K < 2^31, 40*K < 2^31), W4A8_ALGO_MFMA_RQ for K > 131072 (the
- * int32 sum must stay exact) or more than 2^31 - 1 tiles of 256 tokens x 192 rows.  An
- * unknown algorithm code returns W4A8_ERR_DTYPE. */
+ * int32 sum must stay exact), and the three prefill GEMMs (MFMA_I8, MFMA_F16, MFMA_RQ) for
+ * more than 2^31 - 1 tiles of 256 tokens x 192 rows.  An unknown algorithm code returns
+ * W4A8_ERR_DTYPE. */
 W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,
