@@ -208,10 +208,10 @@ int orc_lloyd_max16(const float *sample, int64_t S, int max_iters, double *c16,
 }
 
 /* ------------------------------------------------------------------------------------
- * Offline weight quantisation.  [card A "Format": four tensors per layer -- packed int4
- * indices two per byte, fp8 e4m3 scale per 16 values, fp32 scale per output row, fp32
- * codebook of 16 levels; three tiers of scaling: codebook shape, group magnitude, row
- * magnitude; rotation before quantisation.]  Readings:
+ * Offline weight quantisation.  [card A "Format": a layer is stored as four tensors (4-bit
+ * indices packed in bytes, one e4m3 scale per group of 16, one fp32 scale per row, a
+ * 16-entry fp32 codebook); the per-tensor codebook, the per-16 e4m3 scale and the per-row
+ * fp32 scale each carry one factor of a weight; the rotation comes first.]  Readings:
  *   1. rotate each row in 256-blocks (orc_fwht256);
  *   2. s_ch[r] = max_k |w_rot[r,k]|                                   (row magnitude)
  *   3. s_rel[r,g] = e4m3(gmax[r,g] / s_ch[r]), gmax the group's max |w_rot| (fp32 divide;
@@ -318,8 +318,8 @@ void orc_prepare(const float *x, int64_t M, int64_t K, int8_t *xq, float *sx) {
 
 /* ------------------------------------------------------------------------------------
  * Dequantised weight, exact in fp64: w_hat[r,k] = s_ch[r] * dec(s_rel[r,k/16]) *
- * cb[idx[r,k]] (24 + 4 + 24 significant bits fit in 53).  [card A "Format": three tiers
- * of scaling -- codebook shape, group magnitude, row magnitude.]
+ * cb[idx[r,k]] (24 + 4 + 24 significant bits fit in 53).  [card A "Format": a weight is
+ * the product of its codebook level, its group's e4m3 scale and its row's fp32 scale.]
  * ------------------------------------------------------------------------------------ */
 static inline int unpack_idx(const int8_t *packed_row, int64_t k) {
     uint8_t byte = (uint8_t)packed_row[k / 2];
@@ -423,7 +423,7 @@ void orc_linear_i8_ref(const int8_t *xq, const float *sx, int64_t M, int64_t K,
                 }
                 double sg = orc_e4m3_decode(s_rel[r * G + g]);
                 acc += sg * (double)p;
-                a += sg * pabs;
+                a += fabs(sg) * pabs;
                 if (P) P[(ti * nrow + ri) * G + g] = p;
             }
             double scale = (double)sx[m] * (double)s_ch[r] * (double)s_cb;

@@ -437,6 +437,73 @@ def test_linear_i8_partials_exact_and_codebook_properties():
     assert np.all(np.abs(y8 - y8n) <= 1e-12 * A8)
 
 
+def test_int8_codebook_rounding_term_on_sparse_activations():
+    """The int8 route's one approximation beyond fp32 rounding: each codebook level moves to
+    the nearest multiple of s_cb, by at most s_cb / 2.  With one non-zero activation per
+    token nothing averages that out, so each output's error is exactly the rounding of one
+    level times its scales: bounded by s_x * s_ch * |dec(s_rel)| * (s_cb / 2) * |x_q| and
+    equal to s_x * s_ch * dec(s_rel) * |cb_i8 * s_cb - cb| * |x_q| up to the fp64 sums.  On
+    the seed-0 256 x 512 layer that rounding is far outside the 4e-3 * sum |x w| gate for
+    tokens that fall on the smallest levels: the route meets the gate only statistically."""
+    N, K = 256, 512
+    W = S.weights(N, K, seed=0)
+    q = O.quantize_weight(W, seed=0)
+    s_cb, cbi8 = O.codebook_i8(q["cb"])
+    cb = q["cb"].astype(np.float64)
+    lvl_err = np.abs(cbi8.astype(np.float64) * np.float64(s_cb) - cb)
+    assert np.all(lvl_err <= s_cb / 2 * (1 + 1e-6))
+    # one token per column k, with x_q = 127 there and 0 elsewhere; s_x = 1 / 127
+    ks = np.arange(0, K, 7)
+    M = ks.size
+    xq = np.zeros((M, K), np.int8)
+    xq[np.arange(M), ks] = 127
+    sx = np.full(M, np.float32(1.0 / 127.0), np.float32)
+    y, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    y8, _ = O.linear_i8_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    idx = np.empty((N, K), np.int64)
+    idx[:, 0::2] = q["packed"].view(np.uint8) & 15
+    idx[:, 1::2] = q["packed"].view(np.uint8) >> 4
+    dec = e4m3_torch_decode(q["s_rel"])[:, ks // 16].T                 # [M, N]
+    scale = sx.astype(np.float64)[:, None] * q["s_ch"].astype(np.float64)[None, :] * np.abs(dec) * 127
+    want = scale * lvl_err[idx[:, ks].T]                                 # the level's rounding
+    err = np.abs(y8 - y)
+    assert np.all(np.abs(err - want) <= 1e-9 * scale + 1e-300)
+    assert np.all(err <= scale * s_cb / 2 * (1 + 1e-6))
+    # the gate is A-relative; on the smallest levels the rounding exceeds it many times over
+    ratio = err[A > 0] / (4e-3 * A[A > 0])
+    smallest = np.argmin(np.abs(cb))
+    print(f"one-hot x_q: max |y8 - y| / (4e-3 A) = {ratio.max():.2f}; smallest level {cb[smallest]:.4f} "
+          f"moves by {lvl_err[smallest] / abs(cb[smallest]) * 100:.2f}%")
+    assert lvl_err[smallest] / abs(cb[smallest]) > 4e-3
+    assert ratio.max() > 1.0
+
+
+def test_linear_i8_abs_sum_with_signed_scales():
+    """A8, the bound's scale in the int8 route, is the sum over k of |s_x x_q cb_i8 s_cb
+    dec(s_rel) s_ch| term by term, whatever the signs: random layer bytes with every finite
+    group-scale code, the negative ones included, against that sum taken directly."""
+    N, K, M = 12, 512, 3
+    g = np.random.default_rng(4)
+    packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    s_rel = g.choice(codes, size=(N, K // 16))
+    s_ch = (0.01 + 0.02 * g.random(N)).astype(np.float32)
+    cb = np.sort(g.standard_normal(16)).astype(np.float32)
+    xq = g.integers(-127, 128, size=(M, K), dtype=np.int8)
+    sx = (0.01 + g.random(M)).astype(np.float32)
+    y8, A8 = O.linear_i8_ref(xq, sx, packed, s_rel, s_ch, cb)
+    s_cb, cbi8 = O.codebook_i8(cb)
+    idx = np.empty((N, K), np.int64)
+    idx[:, 0::2] = packed.view(np.uint8) & 15
+    idx[:, 1::2] = packed.view(np.uint8) >> 4
+    wsc = (e4m3_torch_decode(s_rel).repeat(16, axis=1) * cbi8.astype(np.float64)[idx]
+           * s_ch.astype(np.float64)[:, None] * np.float64(s_cb))       # [N, K]
+    terms = sx.astype(np.float64)[:, None, None] * xq.astype(np.float64)[:, None, :] * wsc[None]
+    assert np.all(np.abs(A8 - np.abs(terms).sum(-1)) <= 1e-12 * A8)
+    assert np.all(np.abs(y8 - terms.sum(-1)) <= 1e-12 * A8)
+    assert np.any(np.abs(terms.sum(-1)) < 0.5 * A8)   # signs do cancel in y8
+
+
 # Integer codebook with max |level| = 127, so s_cb = 1 exactly and the table entries below
 # are hand values: t[c][j] = level_j * dec(c) rounded half to even, clamped to +-127.
 RQ_CB = np.array([-127, -64, -5, -3, -1, 0, 1, 3, 5, 7, 9, 11, 50, 64, 100, 127], np.float32)
