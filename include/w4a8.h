@@ -65,11 +65,26 @@ typedef enum { W4A8_F32 = 0, W4A8_BF16 = 1 } w4a8_dtype;
 typedef enum {
     W4A8_ALGO_AUTO = 0,       /* pick by M, N, K (what w4a8_linear does): GEMV within its
                                  range for M <= 3, SKINNY for M <= 64, else MFMA_F16 */
-    W4A8_ALGO_GEMV = 1,       /* fp32-codebook streaming GEMV (decode); M <= 4 and M*K <= 40960 */
+    W4A8_ALGO_GEMV = 1,       /* streaming GEMV (decode); M <= 4 and M*K <= 40960.  The
+                                 codebook is read as fp16 pairs (two levels per packed byte),
+                                 each level scaled by the power of two that brings the largest
+                                 into [0.5, 1) and rounded to fp16: a relative error of at most
+                                 2^-11 per level (levels under 2^-14 of the largest: an absolute
+                                 error of at most 2^-25 of that power of two), fp32 sums */
     W4A8_ALGO_MFMA_I8 = 2,    /* int8 MFMA on the int8 form of the codebook, exact int32
-                                 per-16 partials, fp32 group-scale fold */
-    W4A8_ALGO_MFMA_F16 = 3,   /* f16 MFMA on decoded weights (codebook x group scale in f16),
-                                 128 x 256 tiles (prefill) */
+                                 per-16 partials, fp32 group-scale fold.  The int8 codebook is
+                                 cb_i8 = rint(codebook / s_cb), s_cb = max|codebook| / 127, so
+                                 each level moves by up to s_cb / 2: on top of the fp32 fold the
+                                 output carries up to s_x * s_channel * sum_g |dec(s_rel)| *
+                                 (s_cb / 2) * sum_{k in g} |x_q|.  That term is not inside the
+                                 4e-3 bound of w4a8_linear for every input (activations that
+                                 fall on small levels only can exceed it); dense activations
+                                 meet the bound with a wide margin.  An explicit choice, never
+                                 the automatic one */
+    W4A8_ALGO_MFMA_F16 = 3,   /* f16 MFMA on decoded weights: fp16(codebook level x 2^-ex) times
+                                 fp16(dec(s_rel) x 2^7) rounded to fp16 (at most 2^-10 relative
+                                 per weight), fp32 accumulation; 256 x 192 tiles, one workgroup
+                                 per tile (prefill) */
     W4A8_ALGO_MFMA_SKINNY = 4, /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
                                  16-row weight tiles streamed once, M*K < 2^31 */
     W4A8_ALGO_MFMA_RQ = 5     /* full-rate int8 MFMA on requantised weights (prefill):
@@ -77,7 +92,9 @@ typedef enum {
                                  / 127, clamped to +-127, one int32 sum per output,
                                  y = ((float)sum * (s_channel * s_cb)) * s_x; K <= 131072.
                                  Weight rounding to the step s_cb is the only approximation
-                                 (card A "Why this exists": int8 GEMM + dequantisation step) */
+                                 (card A "Why this exists": int8 GEMM + dequantisation step);
+                                 like MFMA_I8 an explicit choice whose error is not inside the
+                                 4e-3 bound for every input */
 } w4a8_algo;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -136,7 +153,7 @@ W4A8_API int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int6
 /*
  * The quantised product [card "...w4a8-convrot-ComfyUI", sections "Why this exists"
  * and "Format": the layer runs on the int8 GEMM path with a codebook dequantisation step
- * on top; three tiers of scaling -- codebook, group, row].
+ * on top; a weight is its codebook level times its group's scale times its row's scale].
  *
  *  x_q, s_x   prepared activations [M][K], [M] (from w4a8_prepare_activation)
  *  packed, s_rel, s_channel, codebook   one layer, layouts as above, N rows
@@ -144,8 +161,11 @@ W4A8_API int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int6
  *  M >= 1, N >= 1, K >= 256, K % 256 == 0
  *
  * Each output satisfies |y - y_exact| <= 4e-3 * sum_k |s_x x_q[k] w_hat[k]| where y_exact
- * is the fp64 value of the formula above (bf16 output adds its own rounding).  Output is
- * deterministic: no atomics, fixed reduction order for a given (M, N, K, algorithm).
+ * is the fp64 value of the formula above (bf16 output adds its own rounding), for any group
+ * scale byte except the two NaN codes (0x7F, 0xFF), and for codebook levels no smaller in
+ * magnitude than 2^-12 of the largest (the fp16 forms of smaller levels carry an absolute
+ * rather than a relative error; such levels contribute correspondingly little).  Output
+ * is deterministic: no atomics, fixed reduction order for a given (M, N, K, algorithm).
  */
 W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
                 const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,

@@ -511,3 +511,138 @@ def test_safetensors_round_trip_on_gpu(w, tmp_path):
     y1, y2 = w.forward(x, L), w.forward(x, L2)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ----------------------------------------------------------------------------- scale codes
+
+def random_layer(N, K, seed, codes):
+    """Layer bytes drawn uniformly: packed indices, group-scale bytes from `codes`, row scales
+    in [0.01, 0.03], a sorted normal codebook (the product is defined by the four tensors)."""
+    g = np.random.default_rng(seed)
+    packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
+    s_rel = g.choice(np.asarray(codes, dtype=np.uint8), size=(N, K // 16))
+    s_ch = (0.01 + 0.02 * g.random(N)).astype(np.float32)
+    cb = np.sort(g.standard_normal(16)).astype(np.float32)
+    return packed, s_rel, s_ch, cb
+
+
+# every e4m3 code but the two NaN codes: subnormal scales 0x01-0x07 (which the quantiser
+# writes for groups under 2^-6 of the row maximum), scales above 1 up to 448 (0x39-0x7E,
+# which the format's relative scale never reaches but a producer may write), and negative
+# codes 0x80-0xFE
+ALL_FINITE_CODES = [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+@pytest.mark.parametrize("algo,N,K,M", [("gemv", 300, 1024, 1), ("gemv", 257, 2048, 3),
+                                        ("mfma_skinny", 300, 1024, 8), ("mfma_skinny", 1001, 768, 64),
+                                        ("mfma_i8", 300, 1024, 300), ("mfma_f16", 300, 1024, 300),
+                                        ("mfma_i8", 200, 768, 8), ("mfma_f16", 200, 768, 8)])
+def test_every_scale_code(w, algo, N, K, M):
+    """Random group-scale bytes over every finite E4M3FN code (each appears over a hundred
+    times) through each kernel that decodes them with the hardware conversion, against the
+    oracle's exact product; the int8 route also against its int8-codebook reading."""
+    a = {"gemv": w.ALGO_GEMV, "mfma_skinny": w.ALGO_MFMA_SKINNY, "mfma_i8": w.ALGO_MFMA_I8,
+         "mfma_f16": w.ALGO_MFMA_F16}[algo]
+    say(f"{algo} every scale code N={N} K={K} M={M}")
+    packed, s_rel, s_ch, cb = random_layer(N, K, 21 + M, ALL_FINITE_CODES)
+    assert len(np.unique(s_rel)) == len(ALL_FINITE_CODES)
+    _, xq, sx = oracle_acts(M, K, 31, 2)
+    L = w.QuantizedLinear(gpu(packed), gpu(s_rel), gpu(s_ch), gpu(cb))
+    y = w.linear(gpu(xq), gpu(sx), L, algo=a)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb)
+    assert_gate(y, yr, A)
+    if algo == "mfma_i8":
+        i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, None, None)
+
+
+# ----------------------------------------------------------------------------- benchmarked launches
+
+def test_bench_gate_up_launch_full_size(w):
+    """The benchmark's dominant launch as it runs there: w4a8_forward_multi over gate and up
+    (two 17408 x 5120 layers, one launch), fp32 activations of one token with 0.1% outlier
+    channels.  x_q and s_x bit-exact; 2048 sampled rows of each layer within the bound."""
+    (N, K) = S.MLP_GATE_UP
+    say(f"bench launch: forward_multi gate+up 2 x {N}x{K}, M=1, fp32 x")
+    qs = [oracle_layer(N, K, 0)[1], oracle_layer(N, K, 1)[1]]
+    x = S.activations(1, K, seed=0)
+    xq_ref, sx_ref = O.prepare(x)
+    Ls = [gpu_layer(w, q) for q in qs]
+    x_q = torch.empty((1, K), dtype=torch.int8, device=DEV)
+    s_x = torch.empty((1,), dtype=torch.float32, device=DEV)
+    ys = w.forward_multi(gpu(x), Ls, x_q=x_q, s_x=s_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(x_q.cpu().numpy(), xq_ref)
+    for g, q in enumerate(qs):
+        rows = sample(N, 2048, 100 + g)
+        y = ys[g].cpu().numpy().astype(np.float64)[:, rows]
+        yr, A = O.linear_ref(xq_ref, sx_ref, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, None)
+        assert_gate(y, yr, A)
+
+
+def test_bench_down_launch_full_size(w):
+    """The benchmark's second launch: w4a8_forward over down (5120 x 17408), fp32
+    activations of one token; x_q and s_x bit-exact, 2048 sampled rows within the bound."""
+    (N, K) = S.MLP_DOWN
+    say(f"bench launch: forward down {N}x{K}, M=1, fp32 x")
+    _, q = oracle_layer(N, K, 0)
+    x = S.activations(1, K, seed=1)
+    xq_ref, sx_ref = O.prepare(x)
+    x_q = torch.empty((1, K), dtype=torch.int8, device=DEV)
+    s_x = torch.empty((1,), dtype=torch.float32, device=DEV)
+    y = w.forward(gpu(x), gpu_layer(w, q), x_q=x_q, s_x=s_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(x_q.cpu().numpy(), xq_ref)
+    rows = sample(N, 2048, 102)
+    yr, A = O.linear_ref(xq_ref, sx_ref, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, None)
+    assert_gate(y.cpu().numpy().astype(np.float64)[:, rows], yr, A)
+
+
+# ----------------------------------------------------------------------------- binding checks
+
+def test_binding_refuses_wrong_buffers(w):
+    """Caller-supplied outputs of the wrong shape are refused before anything is launched
+    (the C ABI cannot see buffer sizes), and the outputs keep their contents."""
+    say("binding refuses undersized and misshapen buffers")
+    N, K, M = 256, 512, 4
+    _, q = oracle_layer(N, K)
+    _, xq, sx = oracle_acts(M, K)
+    L = gpu_layer(w, q)
+    xg, sg = gpu(xq), gpu(sx)
+    x = gpu(S.activations(M, K, seed=3))
+    short_y = torch.full((M, N - 1), 7.0, device=DEV)
+    with pytest.raises(ValueError):
+        w.linear(xg, sg, L, out=short_y)
+    with pytest.raises(ValueError):
+        w.linear(xg, sg, L, out=torch.empty((N, M), device=DEV))
+    with pytest.raises(ValueError):
+        w.forward(x, L, out=short_y)
+    with pytest.raises(ValueError):
+        w.forward(x, L, x_q=torch.empty((M, K - 16), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):
+        w.forward(x, L, s_x=torch.empty((M - 1,), device=DEV))
+    with pytest.raises(ValueError):
+        w.prepare_activation(x, out=(torch.empty((M, K // 2), dtype=torch.int8, device=DEV),
+                                     torch.empty((M,), device=DEV)))
+    with pytest.raises(ValueError):
+        w.prepare_activation(x, out=(torch.empty((M, K), dtype=torch.int8, device=DEV),
+                                     torch.empty((M + 1,), device=DEV)))
+    with pytest.raises(ValueError):
+        w.linear_multi(xg, sg, [L, L], outs=[torch.empty((M, N), device=DEV), short_y])
+    with pytest.raises(ValueError):
+        w.forward_multi(x, [L, L], outs=[short_y, torch.empty((M, N), device=DEV)])
+    with pytest.raises(ValueError):
+        w.forward_multi(x, [L], x_q=torch.empty((1, K), dtype=torch.int8, device=DEV))
+    with pytest.raises(ValueError):   # a layer tensor of the wrong length
+        w.linear(xg, sg, w.QuantizedLinear(L.packed, L.s_rel, L.s_channel[:-1], L.codebook))
+    W8 = w.w8a8_quantize_weight(gpu(S.weights(N, K, seed=1)))
+    with pytest.raises(ValueError):
+        w.w8a8_linear(xg, sg, W8, out=short_y)
+    x_cpu = torch.empty((M, K), dtype=torch.int8)
+    with pytest.raises(ValueError):
+        w.linear(x_cpu, sg, L)
+    torch.cuda.synchronize()
+    assert torch.all(short_y == 7.0)

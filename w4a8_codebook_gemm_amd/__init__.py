@@ -90,16 +90,34 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None, device=None) -> int:
+    """Device pointer of t after checking what the C ABI cannot see: placement, dtype,
+    contiguity and, where given, the exact shape and the device every operand of the call
+    must share (the kernels write M*N or M*K elements into an output buffer whatever its
+    real size, so a short buffer is refused here, before anything is launched)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call's other operands on {device}")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _layer_ptrs(L, k: int, dev, what: str = "layer"):
+    """The four tensors of one layer, checked against in_features k and the call's device."""
+    n = L.packed.shape[0] if L.packed.dim() == 2 else -1
+    return (n,
+            _dev(L.packed, f"{what}.packed", (torch.int8,), (n, k // 2), dev),
+            _dev(L.s_rel, f"{what}.s_rel", (torch.uint8,), (n, k // 16), dev),
+            _dev(L.s_channel, f"{what}.s_channel", (torch.float32,), (n,), dev),
+            _dev(L.codebook, f"{what}.codebook", (torch.float32,), (16,), dev))
 
 
 def _fdtype(t: torch.Tensor) -> int:
@@ -145,19 +163,22 @@ def quantize_weight(w: torch.Tensor, seed: int = 0, workspace: torch.Tensor | No
     n, k = w.shape
     wp = _dev(w, "w", (torch.float32, torch.bfloat16))
     dev = w.device
-    packed = torch.empty((n, k // 2), dtype=torch.int8, device=dev)
-    s_rel = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
-    s_ch = torch.empty((n,), dtype=torch.float32, device=dev)
-    cb = torch.empty((16,), dtype=torch.float32, device=dev)
-    need = quantize_weight_workspace(n, k)
-    if need == 0:
-        _check(2, "w4a8_quantize_weight")
-    if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
-    _check(lib().w4a8_quantize_weight(wp, _fdtype(w), n, k, seed & (2**64 - 1), packed.data_ptr(),
-                                      s_rel.data_ptr(), s_ch.data_ptr(), cb.data_ptr(),
-                                      _dev(workspace, "workspace", (torch.uint8,)),
-                                      workspace.numel(), _stream()), "w4a8_quantize_weight")
+    with torch.cuda.device(dev):
+        packed = torch.empty((n, k // 2), dtype=torch.int8, device=dev)
+        s_rel = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        s_ch = torch.empty((n,), dtype=torch.float32, device=dev)
+        cb = torch.empty((16,), dtype=torch.float32, device=dev)
+        need = quantize_weight_workspace(n, k)
+        if need == 0:
+            _check(2, "w4a8_quantize_weight")
+        if workspace is None:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        if workspace.dim() != 1:
+            raise ValueError("workspace must be 1-D")
+        _check(lib().w4a8_quantize_weight(wp, _fdtype(w), n, k, seed & (2**64 - 1), packed.data_ptr(),
+                                          s_rel.data_ptr(), s_ch.data_ptr(), cb.data_ptr(),
+                                          _dev(workspace, "workspace", (torch.uint8,), None, dev),
+                                          workspace.numel(), _stream()), "w4a8_quantize_weight")
     return QuantizedLinear(packed, s_rel, s_ch, cb)
 
 
@@ -167,14 +188,16 @@ def prepare_activation(x: torch.Tensor, out=None):
         raise ValueError("x must be 2-D [M, K]")
     m, k = x.shape
     xp = _dev(x, "x", (torch.float32, torch.bfloat16))
+    dev = x.device
     if out is None:
-        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
-        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
+        x_q = torch.empty((m, k), dtype=torch.int8, device=dev)
+        s_x = torch.empty((m,), dtype=torch.float32, device=dev)
     else:
         x_q, s_x = out
-    _check(lib().w4a8_prepare_activation(xp, _fdtype(x), m, k, _dev(x_q, "x_q", (torch.int8,)),
-                                         _dev(s_x, "s_x", (torch.float32,)), _stream()),
-           "w4a8_prepare_activation")
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_prepare_activation(xp, _fdtype(x), m, k, _dev(x_q, "x_q", (torch.int8,), (m, k), dev),
+                                             _dev(s_x, "s_x", (torch.float32,), (m,), dev), _stream()),
+               "w4a8_prepare_activation")
     return x_q, s_x
 
 
@@ -185,23 +208,19 @@ def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dty
     algo: ALGO_AUTO (what w4a8_linear picks), ALGO_GEMV, ALGO_MFMA_SKINNY, ALGO_MFMA_F16,
     ALGO_MFMA_I8 (exact per-16 fold) or ALGO_MFMA_RQ (weights requantised to int8: an
     approximation of the product, see w4a8.h)."""
+    if x_q.dim() != 2:
+        raise ValueError("x_q must be 2-D [M, K]")
     m, k = x_q.shape
-    n = layer.packed.shape[0]
-    if (tuple(layer.packed.shape) != (n, k // 2) or tuple(layer.s_rel.shape) != (n, k // 16)
-            or tuple(layer.s_channel.shape) != (n,) or tuple(layer.codebook.shape) != (16,)
-            or tuple(s_x.shape) != (m,)):
-        raise ValueError(f"inconsistent shapes: x_q {tuple(x_q.shape)}, s_x {tuple(s_x.shape)}, "
-                         f"packed {tuple(layer.packed.shape)}, s_rel {tuple(layer.s_rel.shape)}, "
-                         f"s_channel {tuple(layer.s_channel.shape)}, codebook {tuple(layer.codebook.shape)}")
+    dev = x_q.device
+    xqp = _dev(x_q, "x_q", (torch.int8,))
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    n, pp, sp, cp, bp = _layer_ptrs(layer, k, dev)
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=x_q.device)
-    yp = _dev(out, "y", (torch.float32, torch.bfloat16))
-    _check(lib().w4a8_linear_algo(
-        _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
-        _dev(layer.packed, "packed", (torch.int8,)), _dev(layer.s_rel, "s_rel", (torch.uint8,)),
-        _dev(layer.s_channel, "s_channel", (torch.float32,)),
-        _dev(layer.codebook, "codebook", (torch.float32,)), n, yp, _fdtype(out), algo, _stream()),
-        "w4a8_linear")
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    yp = _dev(out, "y", (torch.float32, torch.bfloat16), (m, n), dev)
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_linear_algo(xqp, sxp, m, k, pp, sp, cp, bp, n, yp, _fdtype(out), algo, _stream()),
+               "w4a8_linear")
     return out
 
 
@@ -212,45 +231,38 @@ def forward(x: torch.Tensor, layer: QuantizedLinear, out_dtype=torch.float32, ou
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     m, k = x.shape
-    n = layer.packed.shape[0]
-    if (tuple(layer.packed.shape) != (n, k // 2) or tuple(layer.s_rel.shape) != (n, k // 16)
-            or tuple(layer.s_channel.shape) != (n,) or tuple(layer.codebook.shape) != (16,)):
-        raise ValueError("layer tensors do not match x's in_features")
+    dev = x.device
     xp = _dev(x, "x", (torch.float32, torch.bfloat16))
+    n, pp, sp, cp, bp = _layer_ptrs(layer, k, dev)
     if x_q is None:
-        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        x_q = torch.empty((m, k), dtype=torch.int8, device=dev)
     if s_x is None:
-        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
+        s_x = torch.empty((m,), dtype=torch.float32, device=dev)
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    _check(lib().w4a8_forward(xp, _fdtype(x), m, k, _dev(layer.packed, "packed", (torch.int8,)),
-                              _dev(layer.s_rel, "s_rel", (torch.uint8,)),
-                              _dev(layer.s_channel, "s_channel", (torch.float32,)),
-                              _dev(layer.codebook, "codebook", (torch.float32,)), n,
-                              _dev(out, "y", (torch.float32, torch.bfloat16)), _fdtype(out),
-                              _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)),
-                              _stream()), "w4a8_forward")
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    yp = _dev(out, "y", (torch.float32, torch.bfloat16), (m, n), dev)
+    xqp = _dev(x_q, "x_q", (torch.int8,), (m, k), dev)
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_forward(xp, _fdtype(x), m, k, pp, sp, cp, bp, n, yp, _fdtype(out), xqp, sxp,
+                                  _stream()), "w4a8_forward")
     return out
 
 
-def _layer_table(layers, m, k, out_dtype, outs):
+def _layer_table(layers, m, k, out_dtype, outs, dev):
     if not 1 <= len(layers) <= MAX_GROUP:
         raise ValueError(f"1 to {MAX_GROUP} layers per call, got {len(layers)}")
     if outs is None:
         outs = [None] * len(layers)
+    if len(outs) != len(layers):
+        raise ValueError(f"{len(layers)} layers but {len(outs)} outputs")
     table = (Layer * len(layers))()
     ys = []
     for g, (L, y) in enumerate(zip(layers, outs)):
-        n = L.packed.shape[0]
-        if (tuple(L.packed.shape) != (n, k // 2) or tuple(L.s_rel.shape) != (n, k // 16)
-                or tuple(L.s_channel.shape) != (n,) or tuple(L.codebook.shape) != (16,)):
-            raise ValueError(f"layer {g}: tensors do not match in_features {k}")
+        n, pp, sp, cp, bp = _layer_ptrs(L, k, dev, f"layer {g}")
         if y is None:
-            y = torch.empty((m, n), dtype=out_dtype, device=L.packed.device)
-        table[g] = Layer(_dev(L.packed, "packed", (torch.int8,)), _dev(L.s_rel, "s_rel", (torch.uint8,)),
-                         _dev(L.s_channel, "s_channel", (torch.float32,)),
-                         _dev(L.codebook, "codebook", (torch.float32,)), n,
-                         _dev(y, "y", (torch.float32, torch.bfloat16)))
+            y = torch.empty((m, n), dtype=out_dtype, device=dev)
+        table[g] = Layer(pp, sp, cp, bp, n, _dev(y, f"y of layer {g}", (torch.float32, torch.bfloat16), (m, n), dev))
         ys.append(y)
     dt = {_fdtype(y) for y in ys}
     if len(dt) != 1:
@@ -260,12 +272,16 @@ def _layer_table(layers, m, k, out_dtype, outs):
 
 def linear_multi(x_q: torch.Tensor, s_x: torch.Tensor, layers, out_dtype=torch.float32, outs=None):
     """The product of prepared activations with several layers (one launch at GEMV sizes)."""
+    if x_q.dim() != 2:
+        raise ValueError("x_q must be 2-D [M, K]")
     m, k = x_q.shape
-    if tuple(s_x.shape) != (m,):
-        raise ValueError("s_x must be [M]")
-    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs)
-    _check(lib().w4a8_linear_multi(_dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
-                                   len(ys), C.addressof(table), ydt, _stream()), "w4a8_linear_multi")
+    dev = x_q.device
+    xqp = _dev(x_q, "x_q", (torch.int8,))
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs, dev)
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_linear_multi(xqp, sxp, m, k, len(ys), C.addressof(table), ydt, _stream()),
+               "w4a8_linear_multi")
     return ys
 
 
@@ -274,15 +290,18 @@ def forward_multi(x: torch.Tensor, layers, out_dtype=torch.float32, outs=None, x
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     m, k = x.shape
+    dev = x.device
     xp = _dev(x, "x", (torch.float32, torch.bfloat16))
     if x_q is None:
-        x_q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+        x_q = torch.empty((m, k), dtype=torch.int8, device=dev)
     if s_x is None:
-        s_x = torch.empty((m,), dtype=torch.float32, device=x.device)
-    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs)
-    _check(lib().w4a8_forward_multi(xp, _fdtype(x), m, k, len(ys), C.addressof(table), ydt,
-                                    _dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)),
-                                    _stream()), "w4a8_forward_multi")
+        s_x = torch.empty((m,), dtype=torch.float32, device=dev)
+    xqp = _dev(x_q, "x_q", (torch.int8,), (m, k), dev)
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    table, ys, ydt = _layer_table(layers, m, k, out_dtype, outs, dev)
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_forward_multi(xp, _fdtype(x), m, k, len(ys), C.addressof(table), ydt, xqp, sxp,
+                                        _stream()), "w4a8_forward_multi")
     return ys
 
 
@@ -307,23 +326,28 @@ def w8a8_quantize_weight(w: torch.Tensor) -> W8Linear:
     wp = _dev(w, "w", (torch.float32, torch.bfloat16))
     w_q = torch.empty((n, k), dtype=torch.int8, device=w.device)
     s_w = torch.empty((n,), dtype=torch.float32, device=w.device)
-    _check(lib().w4a8_w8a8_quantize_weight(wp, _fdtype(w), n, k, w_q.data_ptr(), s_w.data_ptr(), _stream()),
-           "w4a8_w8a8_quantize_weight")
+    with torch.cuda.device(w.device):
+        _check(lib().w4a8_w8a8_quantize_weight(wp, _fdtype(w), n, k, w_q.data_ptr(), s_w.data_ptr(), _stream()),
+               "w4a8_w8a8_quantize_weight")
     return W8Linear(w_q, s_w)
 
 
 def w8a8_linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: W8Linear, out_dtype=torch.float32,
                 algo: int = ALGO_AUTO, out: torch.Tensor | None = None) -> torch.Tensor:
     """y [M, N] of the W8A8 comparator (algo: ALGO_AUTO, ALGO_GEMV or ALGO_MFMA_I8)."""
+    if x_q.dim() != 2:
+        raise ValueError("x_q must be 2-D [M, K]")
     m, k = x_q.shape
-    n = layer.w_q.shape[0]
-    if tuple(layer.w_q.shape) != (n, k) or tuple(layer.s_w.shape) != (n,) or tuple(s_x.shape) != (m,):
-        raise ValueError(f"inconsistent shapes: x_q {tuple(x_q.shape)}, s_x {tuple(s_x.shape)}, "
-                         f"w_q {tuple(layer.w_q.shape)}, s_w {tuple(layer.s_w.shape)}")
+    dev = x_q.device
+    n = layer.w_q.shape[0] if layer.w_q.dim() == 2 else -1
+    xqp = _dev(x_q, "x_q", (torch.int8,))
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    wqp = _dev(layer.w_q, "w_q", (torch.int8,), (n, k), dev)
+    swp = _dev(layer.s_w, "s_w", (torch.float32,), (n,), dev)
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=x_q.device)
-    _check(lib().w4a8_w8a8_linear(_dev(x_q, "x_q", (torch.int8,)), _dev(s_x, "s_x", (torch.float32,)), m, k,
-                                  _dev(layer.w_q, "w_q", (torch.int8,)), _dev(layer.s_w, "s_w", (torch.float32,)),
-                                  n, _dev(out, "y", (torch.float32, torch.bfloat16)), _fdtype(out), algo,
-                                  _stream()), "w4a8_w8a8_linear")
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    yp = _dev(out, "y", (torch.float32, torch.bfloat16), (m, n), dev)
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_w8a8_linear(xqp, sxp, m, k, wqp, swp, n, yp, _fdtype(out), algo, _stream()),
+               "w4a8_w8a8_linear")
     return out
