@@ -57,18 +57,20 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
-FP32_VALU_LANE_OPS = 78.65e12   # fp32 vector peak 157.3 TFLOP/s counts an FMA as two
 
 
-def fold_ceiling_tops():
-    """What the exact per-16 fold allows: every int32 group partial (M N K / 16 of them) takes
-    a conversion and an fma on the vector ALU (two lane operations), and the MFMA that covers
-    one group of 16 (v_mfma_i32_32x32x16_i8) runs at half the int8 peak.  Issued one after the
-    other the two take 2 M N K / (T_valu + T_mfma) with T_valu = (M N K / 8) / FP32_VALU_LANE_OPS
-    and T_mfma = 2 M N K / (peak / 2); the ratio does not depend on M, N or K."""
-    t_valu = (1.0 / 8.0) / FP32_VALU_LANE_OPS          # per multiply-accumulate
+def fold_ceiling_tops(valu_lane_ops):
+    """What the exact per-16 fold allows, from the measured vector-ALU rate of its two
+    instructions (v_cvt_f32_i32 + v_fmac_f32 per int32 group partial, lane operations per
+    second at the int8 kernel's two waves per SIMD; packed fp32 is off and the conversion has
+    no packed form).  Per multiply-accumulate the fold costs 2 / 16 lane operations:
+    T_valu = (1 / 8) / R.  The MFMA that covers one group of 16 (v_mfma_i32_32x32x16_i8) runs
+    at half the int8 peak: T_mfma = 2 / (peak / 2).  Returns (overlapped, serial) TOP/s:
+    2 / max(T_valu, T_mfma) if the two units run side by side from different waves (the upper
+    bound), 2 / (T_valu + T_mfma) if they take turns; neither depends on M, N or K."""
+    t_valu = (1.0 / 8.0) / valu_lane_ops
     t_mfma = 2.0 / (INT8_PEAK_TOPS * 1e12 / 2.0)
-    return 2.0 / (t_valu + t_mfma) / 1e12
+    return 2.0 / max(t_valu, t_mfma) / 1e12, 2.0 / (t_valu + t_mfma) / 1e12
 COPIES = 8
 METRIC = "W4A8 linear: effective weight GB/s (M=1) + int8 TOPS (M=2048) on 1 MI355X"
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
@@ -150,35 +152,81 @@ def make_graph(torch, fn):
     return g
 
 
-def read_ceiling(torch, nbytes, copies=COPIES):
-    """The achievable HBM read rate at nbytes per launch: a plain streaming read (the helper
-    kernel of bench_read.hip) over `copies` distinct buffers, as the decode kernels rotate
-    through weight copies; the best of three grid sizes.  None when the helper is not built."""
-    path = os.path.join(ROOT, "bench_read.so")
-    if not os.path.exists(path):
+PROBES = os.path.join(ROOT, "bench_probes.so")
+
+
+def probes():
+    """The measurement helpers of bench_probes.hip (built by __graft_entry__.build()), or
+    None when they are not built."""
+    if not os.path.exists(PROBES):
         return None
-    lib = ctypes.CDLL(path)
+    lib = ctypes.CDLL(PROBES)
     lib.bench_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
-                                      ctypes.c_void_p]
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.bench_read_launch.restype = ctypes.c_int
+    lib.bench_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bench_valu_launch.restype = ctypes.c_int
+    return lib
+
+
+def read_ceiling(torch, nbytes, copies=COPIES):
+    """The achievable HBM read rate at nbytes per launch: a plain streaming read (non-temporal
+    16-byte loads, each workgroup on a contiguous share) over `copies` distinct buffers, as
+    the decode kernels rotate through weight copies, timed like the kernels.  The best over
+    workgroup widths 256 / 512 / 1024 threads, 2 / 4 / 8 loads in flight per thread and one or
+    two workgroups per compute unit.  Returns (GB/s, config) or None when the helper is not
+    built."""
+    lib = probes()
+    if lib is None:
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     n = nbytes // 16 * 16
     bufs = [torch.full((n,), c + 1, dtype=torch.uint8, device="cuda") for c in range(copies)]
-    best = 0.0
-    for blocks in (256, 512, 1024):
-        sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(2 * cus * 1024, dtype=torch.int32, device="cuda")
+    best, cfg = 0.0, None
+    for per_cu in (1, 2):
+        for threads in (256, 512, 1024):
+            for depth in (2, 4, 8):
+                blocks = per_cu * cus
 
-        def launch():
-            st = torch.cuda.current_stream().cuda_stream
-            for b in bufs:
-                rc = lib.bench_read_launch(b.data_ptr(), n, sink.data_ptr(), blocks, st)
-                if rc != 0:
-                    raise RuntimeError(f"bench_read_launch: HIP error {rc}")
-        g = make_graph(torch, launch)
-        t = time_kernel_graph(torch, g) / copies
-        best = max(best, n / t / 1e9)
+                def launch():
+                    st = torch.cuda.current_stream().cuda_stream
+                    for b in bufs:
+                        rc = lib.bench_read_launch(b.data_ptr(), n, sink.data_ptr(), blocks, threads, depth, st)
+                        if rc != 0:
+                            raise RuntimeError(f"bench_read_launch: HIP error {rc}")
+                g = make_graph(torch, launch)
+                t = time_kernel_graph(torch, g) / copies
+                if n / t / 1e9 > best:
+                    best, cfg = n / t / 1e9, dict(workgroups_per_cu=per_cu, threads=threads,
+                                                  loads_in_flight_per_thread=depth,
+                                                  kib_in_flight_per_cu=per_cu * threads * depth * 16 // 1024,
+                                                  us_per_launch=round(t * 1e6, 3))
+                del g
     del bufs
     torch.cuda.empty_cache()
-    return best
+    return best, cfg
+
+
+def valu_rate(torch, iters=4096):
+    """Lane operations per second of the int8 fold's instruction pair (v_cvt_f32_i32 +
+    v_fmac_f32, 16 independent accumulators per thread) with one 512-thread workgroup per
+    compute unit, i.e. two waves per SIMD (the helper kernel of bench_probes.hip)."""
+    lib = probes()
+    if lib is None:
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus * 512, dtype=torch.float32, device="cuda")
+
+    def launch():
+        st = torch.cuda.current_stream().cuda_stream
+        for _ in range(4):
+            rc = lib.bench_valu_launch(cus, iters, sink.data_ptr(), st)
+            if rc != 0:
+                raise RuntimeError(f"bench_valu_launch: HIP error {rc}")
+    g = make_graph(torch, launch)
+    t = time_kernel_graph(torch, g) / 4
+    return cus * 512 * iters * 32 / t
 
 
 def busy(torch):
@@ -291,16 +339,17 @@ def decode(w, torch, S, args, shapes):
         w.linear(*xq_hid, b["down"], out=y_dn)
 
     full = make_graph(torch, lambda: [step(c) for c in range(COPIES)])
-    rem = args.steps % COPIES
-    tail = make_graph(torch, lambda: [step(c) for c in range(rem)]) if rem else None
+    tails = {r: make_graph(torch, lambda: [step(c) for c in range(r)])
+             for r in {args.steps % COPIES, args.warmup % COPIES} if r}
 
     def run(nsteps):
+        """Exactly nsteps steps: whole graphs of COPIES steps, then a graph of the rest."""
         for _ in range(nsteps // COPIES):
             full.replay()
         if nsteps % COPIES:
-            tail.replay()
+            tails[nsteps % COPIES].replay()
 
-    warm = args.warmup - args.warmup % COPIES
+    warm = args.warmup
     run(warm)
     torch.cuda.synchronize()
     busy(torch)
@@ -335,12 +384,14 @@ def decode(w, torch, S, args, shapes):
                     kernel="k_gemv<1,1,8> (fused rotate + quantise + W4A8 GEMV of gate and up, fp32 x)",
                     per_launch_bytes=int(per_gu), avg_launch_us=round(t_gu * 1e6, 3),
                     avg_launch_us_sustained=round(t_gu_sustained * 1e6, 3))
-    rc = read_ceiling(torch, int(per_gu))
-    if rc:
+    rcc = read_ceiling(torch, int(per_gu))
+    if rcc:
+        rc, cfg = rcc
         roofline["read_ceiling_gbs"] = round(rc, 1)
+        roofline["read_ceiling_config"] = cfg
         roofline["frac_of_read_ceiling"] = round(ach / rc, 4)
-        log(f"plain read of {per_gu / 1e6:.1f} MB per launch: {rc:.1f} GB/s; the fused gate+up launch "
-            f"reaches {ach / rc * 100:.1f}% of it")
+        log(f"plain read of {per_gu / 1e6:.1f} MB per launch: {rc:.1f} GB/s ({cfg}); the fused gate+up "
+            f"launch reaches {ach / rc * 100:.1f}% of it")
     down_k = dict(kernel="k_gemv<1,1,1> (fused rotate + quantise + W4A8 GEMV of down, fp32 x)",
                   avg_launch_us=round(t_dn * 1e6, 3), per_launch_bytes=int(per_dn),
                   achieved=round(per_dn / t_dn / 1e9, 1), frac=round(per_dn / t_dn / 1e9 / HBM_PEAK_GBS, 4))
@@ -492,10 +543,43 @@ def prefill(w, torch, S, shapes, M=2048):
         mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
         summary[name] = dict(tops=round(mean, 1), roofline=dict(
             bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
-    fc = fold_ceiling_tops()
-    summary["mfma_i8"]["fold_ceiling"] = dict(tops=round(fc, 1), frac=round(summary["mfma_i8"]["tops"] / fc, 4))
+    r = valu_rate(torch)
+    if r:
+        fc, fs = fold_ceiling_tops(r)
+        summary["mfma_i8"]["fold_ceiling"] = dict(
+            valu_lane_ops_per_s=round(r / 1e12, 2), unit="TOP/s", tops=round(fc, 1), serial_tops=round(fs, 1),
+            frac=round(summary["mfma_i8"]["tops"] / fc, 4), frac_of_serial=round(summary["mfma_i8"]["tops"] / fs, 4))
+        log(f"fold instruction pair at two waves per SIMD: {r / 1e12:.2f} T lane operations/s; fold ceiling "
+            f"{fc:.0f} TOP/s overlapped with the MFMA, {fs:.0f} TOP/s taking turns")
     del pl
-    return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, **summary)
+    torch.cuda.empty_cache()
+    return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, prepare=prepare_rate(w, torch, S, M), **summary)
+
+
+def prepare_bytes(m, k, in_bytes=4):
+    """Algorithmic HBM bytes of one activation-preparation launch: x in, x_q and s_x out."""
+    return m * k * in_bytes + m * k + 4 * m
+
+
+def prepare_rate(w, torch, S, M, ks=(5120, 17408)):
+    """The activation preparation (k_prepare: rotation + per-token int8) at prefill size, fp32
+    input, over COPIES distinct input buffers (larger in all than the Infinity Cache), timed
+    like the decode kernels; HBM-bound: 5 K + 4 bytes per token."""
+    res = {}
+    for k in ks:
+        xs = [torch.from_numpy(S.activations(M, k, seed=c)).cuda() for c in range(COPIES)]
+        x_q = torch.empty((M, k), dtype=torch.int8, device="cuda")
+        s_x = torch.empty((M,), dtype=torch.float32, device="cuda")
+        g = make_graph(torch, lambda: [w.prepare_activation(x, out=(x_q, s_x)) for x in xs])
+        t = time_kernel_graph(torch, g) / COPIES
+        byt = prepare_bytes(M, k)
+        res[f"{M}x{k}"] = dict(kernel="k_prepare (fp32 x)", us=round(t * 1e6, 2), per_launch_bytes=byt,
+                               roofline=dict(bound="hbm", achieved=round(byt / t / 1e9, 1), peak=HBM_PEAK_GBS,
+                                             unit="GB/s", frac=round(byt / t / 1e9 / HBM_PEAK_GBS, 4)))
+        log(f"prepare M={M} K={k}: {t * 1e6:.2f} us, {byt / t / 1e9:.1f} GB/s")
+        del xs, g
+        torch.cuda.empty_cache()
+    return res
 
 
 def quantize_rate(w, torch, S, shapes, reps=3):

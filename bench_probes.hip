@@ -1,0 +1,112 @@
+// Measurement helpers for bench.py (not part of the library): the ceilings the library's
+// kernels are set beside.
+//
+//  * bench_read_launch: the achievable HBM read rate for a byte count.  One workgroup per
+//    compute unit (or a few) reads a contiguous share of the buffer with non-temporal
+//    16-byte buffer loads, DEPTH loads in flight per thread, and folds what it read into
+//    one word that it stores only in a case that never happens, so the loads cannot be
+//    dropped.  The benchmark sweeps workgroup width, depth and workgroups per unit and keeps
+//    the fastest.
+//  * bench_valu_launch: the vector-ALU rate of the int8 route's group fold, one
+//    v_cvt_f32_i32 and one v_fmac_f32 per int32 partial, on 16 independent accumulators per
+//    thread (the 16 outputs one lane holds of a 32 x 32 MFMA tile), with one 512-thread
+//    workgroup per compute unit: two waves per SIMD, the occupancy of the int8 prefill
+//    kernel.  The LDS request keeps a second workgroup off each unit.
+//
+// Both take device pointers, launch on the given stream and return the HIP error code of
+// the launch.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int THREADS, int DEPTH>
+__global__ __launch_bounds__(THREADS) void k_read(const uint8_t *src, uint64_t n16, uint32_t *sink) {
+    const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;      // 16-byte chunks per workgroup
+    const uint64_t lo = per * blockIdx.x, hi = lo + per < n16 ? lo + per : n16;
+    const uint64_t cnt = hi > lo ? hi - lo : 0;
+    // the workgroup's share as a buffer resource: chunks past its end read as zero
+    const uint64_t bytes = cnt * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(src + lo * 16), (short)0, (int)(bytes < 0x7FFFFFFFull ? bytes : 0x7FFFFFFFull), 0x00020000);
+    uint32_t acc = 0;
+    for (uint64_t i = threadIdx.x; i < cnt; i += (uint64_t)DEPTH * THREADS) {
+        u32x4 v[DEPTH];
+#pragma unroll
+        for (int d = 0; d < DEPTH; d++)
+            v[d] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((i + (uint64_t)d * THREADS) * 16), 0, 2);
+#pragma unroll
+        for (int d = 0; d < DEPTH; d++) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
+    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x * THREADS + threadIdx.x] = acc;  // almost never taken
+}
+
+template <int THREADS, int DEPTH>
+int launch_read(const void *src, uint64_t bytes, uint32_t *sink, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((k_read<THREADS, DEPTH>), dim3((unsigned)blocks), dim3(THREADS), 0, s,
+                       static_cast<const uint8_t *>(src), bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+constexpr int kValuThreads = 512;
+constexpr int kValuChains = 16;
+
+__global__ __launch_bounds__(kValuThreads) void k_valu(int iters, float s, float *sink) {
+    extern __shared__ float pad[];  // sized by the launch to keep one workgroup per unit
+    int p[kValuChains];
+    float acc[kValuChains];
+#pragma unroll
+    for (int c = 0; c < kValuChains; c++) {
+        p[c] = (int)(threadIdx.x * 31 + c);
+        acc[c] = 0.0f;
+    }
+    for (int it = 0; it < iters; it++) {
+        // an empty statement that claims to change the partials keeps each conversion in the
+        // loop (it emits no instruction)
+#pragma unroll
+        for (int c = 0; c < kValuChains; c++) asm volatile("" : "+v"(p[c]));
+#pragma unroll
+        for (int c = 0; c < kValuChains; c++) acc[c] = fmaf(s, (float)p[c], acc[c]);
+    }
+    float t = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kValuChains; c++) t += acc[c];
+    if (t == 1234.5f) {
+        pad[threadIdx.x] = t;
+        sink[blockIdx.x * kValuThreads + threadIdx.x] = pad[threadIdx.x ^ 1];
+    }
+}
+
+}  // namespace
+
+// threads in {256, 512, 1024}, depth in {1, 2, 4, 8}; bytes a multiple of 16, and a
+// workgroup's share below 2 GiB (the buffer resource's range).  Returns -1 for another
+// width or depth.
+extern "C" int bench_read_launch(const void *src, uint64_t bytes, uint32_t *sink, int blocks, int threads,
+                                 int depth, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define W4A8_READ_CASE(T, D) if (threads == T && depth == D) return launch_read<T, D>(src, bytes, sink, blocks, s);
+    W4A8_READ_CASE(256, 1) W4A8_READ_CASE(256, 2) W4A8_READ_CASE(256, 4) W4A8_READ_CASE(256, 8)
+    W4A8_READ_CASE(512, 1) W4A8_READ_CASE(512, 2) W4A8_READ_CASE(512, 4) W4A8_READ_CASE(512, 8)
+    W4A8_READ_CASE(1024, 1) W4A8_READ_CASE(1024, 2) W4A8_READ_CASE(1024, 4) W4A8_READ_CASE(1024, 8)
+#undef W4A8_READ_CASE
+    return -1;
+}
+
+// blocks workgroups of 512 threads, each running `iters` rounds of 16 (convert, fma) pairs
+// per thread; sink holds blocks * 512 floats.  Lane operations per launch:
+// blocks * 512 * iters * 32.
+extern "C" int bench_valu_launch(int blocks, int iters, float *sink, void *stream) {
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_valu),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+        if (e != hipSuccess) return (int)e;
+        attr = true;
+    }
+    hipLaunchKernelGGL(k_valu, dim3((unsigned)blocks), dim3(kValuThreads), 96 * 1024,
+                       static_cast<hipStream_t>(stream), iters, 1.0f / 3.0f, sink);
+    return (int)hipGetLastError();
+}
