@@ -104,8 +104,9 @@ W4A8_API int w4a8_version(void);
 W4A8_API const char *w4a8_status_string(int status);
 
 /*
- * Bytes of device workspace w4a8_quantize_weight needs for an N x K weight
- * (0 if the shape is invalid).
+ * Bytes of device workspace w4a8_quantize_weight needs for an N x K weight (0 if the shape
+ * is invalid): the fit sample's keys and prefix sums, at most 12,583,168 bytes whatever the
+ * shape.
  */
 W4A8_API size_t w4a8_quantize_weight_workspace(int64_t N, int64_t K);
 

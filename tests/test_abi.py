@@ -47,8 +47,16 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_size_and_pick(L):
-    assert L.w4a8_quantize_weight_workspace(256, 512) >= 256 * 512 * 4 + 2048 * 4 + (256 * 512 + 1) * 8
-    assert L.w4a8_quantize_weight_workspace(17408, 5120) >= 17408 * 5120 * 4 + (1 << 20) * 12
+    # the fit sample's uint32 keys (padded to a power of two, at least 2048) and its fp64
+    # prefix sums, each rounded up to 256 bytes: no term grows with N * K past 2^20
+    up = lambda b: (b + 255) // 256 * 256
+    assert L.w4a8_quantize_weight_workspace(256, 512) == up(131072 * 4) + up((131072 + 1) * 8)
+    assert L.w4a8_quantize_weight_workspace(1, 256) == up(2048 * 4) + up(257 * 8)
+    assert L.w4a8_quantize_weight_workspace(300, 768) == up(262144 * 4) + up((300 * 768 + 1) * 8)
+    full = up((1 << 20) * 4) + up(((1 << 20) + 1) * 8)
+    assert full == 12583168
+    assert L.w4a8_quantize_weight_workspace(17408, 5120) == full
+    assert L.w4a8_quantize_weight_workspace(1 << 20, 1 << 16) == full
     for bad in [(0, 512), (4, 4304), (4, 100), (-1, 256), (4, 0)]:
         assert L.w4a8_quantize_weight_workspace(*bad) == 0
     assert L.w4a8_linear_pick(1, 17408, 5120) == w.ALGO_GEMV

@@ -9,11 +9,14 @@
 // Steps, each a kernel on the caller's stream:
 //  1. k_rotate_scale: per row, rotate every 256-block (the same lane-level transform as
 //     the activation kernel), s_channel = max |w_rot|, s_rel = E4M3FN(group max / s_channel)
-//     rounded to nearest even, v = w_rot / (s_channel * dec(s_rel)) -> workspace.
-//  2. k_sample_keys: S = min(N*K, 2^20) fit values (all of them, or positions
-//     floor(u_i * N*K / 2^64) with u_i the i-th SplitMix64 output for `seed`), as uint32
-//     keys whose unsigned order is the fp32 total order (-0 before +0); padded with
-//     0xFFFFFFFF to a power of two.
+//     rounded to nearest even.
+//  2. k_sample_keys: S = min(N*K, 2^20) fit values v = w_rot / (s_channel * dec(s_rel)) --
+//     all of them, or those at positions floor(u_i * N*K / 2^64) with u_i the i-th
+//     SplitMix64 output for `seed` -- as uint32 keys whose unsigned order is the fp32 total
+//     order (-0 before +0); padded with 0xFFFFFFFF to a power of two.  Each wave rotates the
+//     256-block that holds its value (or, with every value taken, a whole block) with the
+//     arithmetic of step 1, so the normalised values are never stored: the workspace holds
+//     only the sample and its prefix sums, at most 12 MiB whatever N and K.
 //  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans).
 //  4. k_prefix: running fp64 sums of the sorted values, accumulated strictly left to
 //     right by one thread (the order fixes the rounding, which the codebook bits depend on).
@@ -21,8 +24,9 @@
 //     thresholds (c_j + c_{j+1}) / 2, cell bounds by binary search over the sorted values,
 //     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
 //     codebook = (float)c.
-//  6. k_assign_pack: idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 },
-//     two indices per byte, even element in the low nibble.
+//  6. k_assign_pack: per row, rotate and normalise again (the arithmetic of steps 1 and 2),
+//     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 }, two indices per
+//     byte, even element in the low nibble.
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -35,46 +39,51 @@ constexpr int64_t kSampleMax = 1LL << 20;
 constexpr int kMaxUpdates = 100;
 constexpr int kSortTile = 2048;
 
+constexpr size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr int64_t pow2_at_least(int64_t s) {
+    int64_t p = kSortTile;
+    while (p < s) p <<= 1;
+    return p;
+}
+
+// Workspace: the sample keys (padded to a power of two) and their fp64 prefix sums.
 struct WsLayout {
-    size_t v_off, keys_off, prefix_off, total;
+    size_t keys_off, prefix_off, total;
     int64_t S, P2;
 };
 
-WsLayout layout(int64_t N, int64_t K) {
+constexpr WsLayout layout_for_sample(int64_t S) {
     WsLayout L{};
-    const int64_t NK = N * K;
-    L.S = NK < kSampleMax ? NK : kSampleMax;
-    int64_t p2 = kSortTile;
-    while (p2 < L.S) p2 <<= 1;
-    L.P2 = p2;
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    L.v_off = 0;
-    L.keys_off = up((size_t)NK * 4);
-    L.prefix_off = L.keys_off + up((size_t)L.P2 * 4);
-    L.total = L.prefix_off + up((size_t)(L.S + 1) * 8);
+    L.S = S;
+    L.P2 = pow2_at_least(S);
+    L.keys_off = 0;
+    L.prefix_off = round256((size_t)L.P2 * 4);
+    L.total = L.prefix_off + round256((size_t)(L.S + 1) * 8);
     return L;
 }
 
-// Group scale, normalised values and the s_rel byte of one 16-group spread over 4 lanes.
-__device__ __forceinline__ void scale_block(float v[4], float rmax, int lane, float *vout,
-                                            uint8_t *srel_out) {
+WsLayout layout(int64_t N, int64_t K) {
+    const int64_t NK = N * K;
+    return layout_for_sample(NK < kSampleMax ? NK : kSampleMax);
+}
+
+// The group-scale code of one 16-group spread over 4 lanes (rotated values v, row max rmax).
+__device__ __forceinline__ uint32_t group_code(const float v[4], float rmax) {
     float g = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     g = fmaxf(g, __shfl_xor(g, 1));
     g = fmaxf(g, __shfl_xor(g, 2));
-    const uint32_t code = (rmax > 0.0f) ? f32_to_e4m3_rne(g / rmax) : 0u;
+    return (rmax > 0.0f) ? f32_to_e4m3_rne(g / rmax) : 0u;
+}
+
+// Normalised values v / (rmax * dec(code)), 0 where that product is 0.
+__device__ __forceinline__ void normalise4(float v[4], float rmax, uint32_t code) {
     const float d = rmax * e4m3_to_f32(code);
-    float4 o;
-    o.x = (d > 0.0f) ? v[0] / d : 0.0f;
-    o.y = (d > 0.0f) ? v[1] / d : 0.0f;
-    o.z = (d > 0.0f) ? v[2] / d : 0.0f;
-    o.w = (d > 0.0f) ? v[3] / d : 0.0f;
-    *reinterpret_cast<float4 *>(vout + 4 * lane) = o;
-    if ((lane & 3) == 0) srel_out[lane >> 2] = (uint8_t)code;
+#pragma unroll
+    for (int q = 0; q < 4; q++) v[q] = (d > 0.0f) ? v[q] / d : 0.0f;
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_rotate_scale(const void *__restrict__ w, int64_t K,
-                                                           float *__restrict__ vout,
                                                            uint8_t *__restrict__ s_rel,
                                                            float *__restrict__ s_ch) {
     __shared__ float red[kWaves];
@@ -118,14 +127,18 @@ __global__ __launch_bounds__(kThreads) void k_rotate_scale(const void *__restric
 #pragma unroll
         for (int i = 0; i < kRegBlocks; i++) {
             const int b = wave + i * kWaves;
-            if (b < nblk) scale_block(keep[i], rmax, lane, vout + row + (int64_t)b * kRot, srow + b * 16);
+            if (b < nblk) {
+                const uint32_t code = group_code(keep[i], rmax);
+                if ((lane & 3) == 0) srow[b * 16 + (lane >> 2)] = (uint8_t)code;
+            }
         }
     } else {
         for (int b = wave; b < nblk; b += kWaves) {
             float v[4];
             load4<BF16>(w, row + (int64_t)b * kRot + 4 * lane, v);
             fwht256_lane4(v, lane);
-            scale_block(v, rmax, lane, vout + row + (int64_t)b * kRot, srow + b * 16);
+            const uint32_t code = group_code(v, rmax);
+            if ((lane & 3) == 0) srow[b * 16 + (lane >> 2)] = (uint8_t)code;
         }
     }
 }
@@ -146,17 +159,42 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__global__ void k_sample_keys(const float *__restrict__ v, int64_t NK, int64_t S, int64_t P2,
-                              uint64_t seed, uint32_t *__restrict__ keys) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= P2) return;
-    uint32_t key = 0xFFFFFFFFu;
-    if (i < S) {
-        int64_t pos = i;
-        if (NK > kSampleMax) pos = (int64_t)__umul64hi(splitmix64_at(seed, (uint64_t)i), (uint64_t)NK);
-        key = f32_to_key(v[pos]);
+// One wave per job.  Sampled (N*K > 2^20): job i is sample i, the value at position
+// floor(u_i * N*K / 2^64); every value (N*K <= 2^20): job i is 256-block i, whose values are
+// samples 256 i .. 256 i + 255 in position order.  Either way the wave rotates the whole
+// 256-block (lane l holds elements 4l .. 4l+3) and normalises with the row's s_channel and
+// the group's s_rel, as k_rotate_scale derived them.  Threads past the last job pad the
+// keys from S to P2.
+constexpr int kSampleWaves = 4;
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * kSampleWaves) void k_sample_keys(
+    const void *__restrict__ w, int64_t K, int64_t NK, int64_t S, int64_t P2, uint64_t seed,
+    const float *__restrict__ s_ch, const uint8_t *__restrict__ s_rel, uint32_t *__restrict__ keys) {
+    const int lane = threadIdx.x & 63;
+    const int64_t job = (int64_t)blockIdx.x * kSampleWaves + (threadIdx.x >> 6);
+    const bool sampled = NK > kSampleMax;
+    const int64_t jobs = sampled ? S : NK / kRot;
+    if (job < jobs) {
+        int64_t pos = job * kRot;
+        if (sampled) pos = (int64_t)__umul64hi(splitmix64_at(seed, (uint64_t)job), (uint64_t)NK);
+        const int64_t r = pos / K, blk0 = (pos - r * K) / kRot * kRot;   // first element of the block
+        float v[4];
+        load4<BF16>(w, r * K + blk0 + 4 * lane, v);
+        fwht256_lane4(v, lane);
+        const uint32_t code = s_rel[r * (K / kGroup) + blk0 / kGroup + (lane >> 2)];
+        normalise4(v, s_ch[r], code);
+        if (sampled) {
+            const int e = (int)(pos - r * K - blk0);                     // the sample's element
+            if ((e >> 2) == lane) keys[job] = f32_to_key(v[e & 3]);
+        } else {
+            uint4 k4 = make_uint4(f32_to_key(v[0]), f32_to_key(v[1]), f32_to_key(v[2]), f32_to_key(v[3]));
+            *reinterpret_cast<uint4 *>(keys + job * kRot + 4 * lane) = k4;
+        }
     }
-    keys[i] = key;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = S + t; i < P2; i += nthreads) keys[i] = 0xFFFFFFFFu;
 }
 
 // Bitonic network: pass (k, j) compares i with i ^ j, ascending where (i & k) == 0.
@@ -262,23 +300,35 @@ __global__ __launch_bounds__(64) void k_lloyd(const uint32_t *__restrict__ keys,
     if (j < kLevels) cb[j] = (float)c[j];
 }
 
-__global__ void k_assign_pack(const float *__restrict__ v, int64_t half_nk,
-                              const float *__restrict__ cb, int8_t *__restrict__ packed) {
+// Per row: rotate and normalise every 256-block again (lane l holds elements 4l .. 4l+3, in
+// group l / 4), take each value's nearest level and pack two indices per byte.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict__ w, int64_t K,
+                                                          const float *__restrict__ s_ch,
+                                                          const uint8_t *__restrict__ s_rel,
+                                                          const float *__restrict__ cb,
+                                                          int8_t *__restrict__ packed) {
     __shared__ double mid[kLevels - 1];
     if (threadIdx.x < kLevels - 1)
         mid[threadIdx.x] = ((double)cb[threadIdx.x] + (double)cb[threadIdx.x + 1]) / 2.0;
     __syncthreads();
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= half_nk) return;
-    const float2 p = reinterpret_cast<const float2 *>(v)[i];
-    const double x0 = p.x, x1 = p.y;
-    int i0 = 0, i1 = 0;
+    const int64_t r = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nblk = (int)(K / kRot);
+    const float rmax = s_ch[r];
+    for (int b = wave; b < nblk; b += kWaves) {
+        float v[4];
+        load4<BF16>(w, r * K + (int64_t)b * kRot + 4 * lane, v);
+        fwht256_lane4(v, lane);
+        normalise4(v, rmax, s_rel[r * (K / kGroup) + b * 16 + (lane >> 2)]);
+        int idx[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < kLevels - 1; j++) {
-        i0 += (x0 > mid[j]) ? 1 : 0;
-        i1 += (x1 > mid[j]) ? 1 : 0;
+        for (int j = 0; j < kLevels - 1; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) idx[q] += ((double)v[q] > mid[j]) ? 1 : 0;
+        const uint16_t two = (uint16_t)((idx[0] | (idx[1] << 4)) | ((idx[2] | (idx[3] << 4)) << 8));
+        *reinterpret_cast<uint16_t *>(packed + r * (K / 2) + (int64_t)b * (kRot / 2) + 2 * lane) = two;
     }
-    packed[i] = (int8_t)(uint8_t)(i0 | (i1 << 4));
 }
 
 }  // namespace
@@ -290,20 +340,25 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
                            void *workspace, hipStream_t stream) {
     const WsLayout L = layout(N, K);
     char *ws = static_cast<char *>(workspace);
-    float *v = reinterpret_cast<float *>(ws + L.v_off);
     uint32_t *keys = reinterpret_cast<uint32_t *>(ws + L.keys_off);
     double *P = reinterpret_cast<double *>(ws + L.prefix_off);
     const int64_t NK = N * K;
     hipError_t e;
 
     if (w_bf16)
-        hipLaunchKernelGGL(k_rotate_scale<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, v, s_rel, s_ch);
+        hipLaunchKernelGGL(k_rotate_scale<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_rel, s_ch);
     else
-        hipLaunchKernelGGL(k_rotate_scale<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, v, s_rel, s_ch);
+        hipLaunchKernelGGL(k_rotate_scale<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_rel, s_ch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    hipLaunchKernelGGL(k_sample_keys, dim3((unsigned)((L.P2 + 255) / 256)), dim3(256), 0, stream, v, NK, L.S,
-                       L.P2, seed, keys);
+    const int64_t jobs = NK > kSampleMax ? L.S : NK / kRot;
+    const unsigned sblocks = (unsigned)((jobs + kSampleWaves - 1) / kSampleWaves);
+    if (w_bf16)
+        hipLaunchKernelGGL(k_sample_keys<true>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
+                           L.P2, seed, s_ch, s_rel, keys);
+    else
+        hipLaunchKernelGGL(k_sample_keys<false>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
+                           L.P2, seed, s_ch, s_rel, keys);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     const unsigned tiles = (unsigned)(L.P2 / kSortTile);
@@ -324,9 +379,12 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_lloyd, dim3(1), dim3(64), 0, stream, keys, P, L.S, cb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t half_nk = NK / 2;
-    hipLaunchKernelGGL(k_assign_pack, dim3((unsigned)((half_nk + 255) / 256)), dim3(256), 0, stream, v, half_nk,
-                       cb, packed);
+    if (w_bf16)
+        hipLaunchKernelGGL(k_assign_pack<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_ch, s_rel, cb,
+                           packed);
+    else
+        hipLaunchKernelGGL(k_assign_pack<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_ch, s_rel, cb,
+                           packed);
     return hipGetLastError();
 }
 
