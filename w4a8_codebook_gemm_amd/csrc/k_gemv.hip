@@ -339,10 +339,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // A ring of kDepth units in flight per lane group; the first loads are issued before
     // the prologue so their HBM latency overlaps the table build.  The scheduling barrier
     // keeps every small operand's load ahead of them; with raw activations (a larger first
-    // request per wave) the workgroup barrier also keeps every wave's small loads ahead of
-    // any wave's weight stream.
+    // request per wave) a bare s_barrier also keeps every wave's small loads ahead of any
+    // wave's weight stream.  It orders the issue only: __syncthreads() would first wait for
+    // every small load to land (s_waitcnt vmcnt(0)), holding the weight stream back by a
+    // whole memory round trip.
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XIN != 0) __syncthreads();
+    if constexpr (XIN != 0) __builtin_amdgcn_s_barrier();
     constexpr int kDepth = depth<MT>();
     Slot cur[kDepth];
     u32x4 pa[kDepth], pb[kDepth];
