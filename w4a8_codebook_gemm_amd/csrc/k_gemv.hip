@@ -34,9 +34,10 @@
 //    partial per (row, block) (odd row stride: conflict-free); eight lanes per row then
 //    sum its partials in a fixed order and apply s_channel (loaded at kernel start), s_x
 //    and the codebook's power-of-two scale.  No atomics: the result is deterministic.
-//  * Start-up: every small operand (codebook, row scales, activations) is requested before
-//    the first weight loads; a request issued behind them would wait for the whole first
-//    wave of weight traffic to drain from HBM before the table could be built.
+//  * Start-up: every small operand (row scales, activations, group scales) is requested
+//    before the first weight loads; a request issued behind them would wait in the in-order
+//    vector load counter for the first weight traffic to drain from HBM before the prologue
+//    could use it.  The codebook is read with scalar loads, outside that counter.
 #include <atomic>
 #include "w4a8_internal.h"
 
@@ -279,18 +280,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv(LinearArgs a, GroupTab<NG> gt
     // weight loads in the in-order load counter, so using them does not wait for the
     // weight prefetch.
     const float sch_mine = (tid >> 3) < nrow ? L.s_ch[r0 + (tid >> 3)] : 0.0f;  // row of the first final-sum pass
-    // The codebook (four 16-byte loads, the same line for every lane) and this wave's
-    // high-nibble level, loaded with the other small operands before the weight stream: a
-    // load issued behind the stream's first requests waits for them to drain from HBM.
-    const __amdgpu_buffer_rsrc_t rs_cb = __builtin_amdgcn_make_buffer_rsrc((void *)L.cb, (short)0, kLevels * 4, 0x00020000);
+    // The codebook and this wave's high-nibble level come through the scalar cache: 64
+    // bytes that are the same for every lane.  As vector loads every lane would fetch the
+    // whole line (64 KiB through the workgroup's load path for 64 bytes), and the table
+    // build would wait, in the in-order vector load counter, behind everything issued
+    // before it; scalar loads use a counter of their own.
+    const __attribute__((address_space(4))) float *cbk = (const __attribute__((address_space(4))) float *)L.cb;
     float cbv[kLevels];
 #pragma unroll
-    for (int q = 0; q < kLevels / 4; q++) {
-        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs_cb, 16 * q, 0, 0);
-        cbv[4 * q] = __uint_as_float(c.x); cbv[4 * q + 1] = __uint_as_float(c.y);
-        cbv[4 * q + 2] = __uint_as_float(c.z); cbv[4 * q + 3] = __uint_as_float(c.w);
-    }
-    const float cb_hi = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_cb, 4 * (tid >> 6), 0, 0));
+    for (int q = 0; q < kLevels; q++) cbv[q] = cbk[q];
+    const float cb_hi = cbk[__builtin_amdgcn_readfirstlane(tid >> 6)];
     float sx_all[MT];
     const uint2 *xq8 = reinterpret_cast<const uint2 *>(a.x_q);
     const int nxc = (int)(MT * (K / 8));
