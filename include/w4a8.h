@@ -134,6 +134,24 @@ W4A8_API int w4a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a8_quantize_weight for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the same kernels and the same
+ * results, bit for bit, with the workspace in a static device array of the library, so the
+ * caller passes no workspace and the call allocates nothing.
+ *
+ *  Arguments as for w4a8_quantize_weight, without workspace / workspace_bytes.
+ *  Scratch: 12,583,168 bytes per device (the workspace of a full 2^20-value fit sample, the
+ *  most any N x K needs), held by each device the library runs on until the process ends.
+ *  A shape whose workspace would exceed it returns W4A8_ERR_WORKSPACE (none does today).
+ *  Every call on one device shares that device's array and leaves its contents behind (the
+ *  kernels overwrite all of it that they read), so calls that overlap on one device -- on
+ *  different streams or from different threads -- race and must be serialised by the caller.
+ */
+W4A8_API int w4a8_quantize_weight_noalloc(const void *w, int w_dtype, int64_t N, int64_t K, uint64_t seed,
+                                          int8_t *packed, uint8_t *s_rel, float *s_channel, float *codebook,
+                                          void *stream);
+
+/*
  * Per-call activation preparation [card "Qwen3.8-27B-W4A8", section "Model Overview":
  * 4-bit weights with int8 activations; card "...w4a8-convrot-ComfyUI", section "Format":
  * the layer executes on int8 GEMM in the rotated basis].

@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 13 and set(names) == set(w.EXPORTS)
+    assert len(names) == 14 and set(names) == set(w.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 

@@ -29,7 +29,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN"
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
            "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
            "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward", "w4a8_linear_multi",
-           "w4a8_forward_multi", "w4a8_w8a8_quantize_weight", "w4a8_w8a8_linear")
+           "w4a8_forward_multi", "w4a8_w8a8_quantize_weight", "w4a8_w8a8_linear",
+           "w4a8_quantize_weight_noalloc")
 MAX_GROUP = 8
 
 
@@ -64,6 +65,8 @@ def lib():
         L.w4a8_quantize_weight_workspace.restype = sz
         L.w4a8_quantize_weight.argtypes = [P, i32, i64, i64, u64, P, P, P, P, P, sz, P]
         L.w4a8_quantize_weight.restype = i32
+        L.w4a8_quantize_weight_noalloc.argtypes = [P, i32, i64, i64, u64, P, P, P, P, P]
+        L.w4a8_quantize_weight_noalloc.restype = i32
         L.w4a8_prepare_activation.argtypes = [P, i32, i64, i64, P, P, P]
         L.w4a8_prepare_activation.restype = i32
         L.w4a8_linear.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i32, P]
@@ -180,6 +183,26 @@ def quantize_weight(w: torch.Tensor, seed: int = 0, workspace: torch.Tensor | No
                                           _dev(workspace, "workspace", (torch.uint8,), None, dev),
                                           workspace.numel(), _stream()), "w4a8_quantize_weight")
     return QuantizedLinear(packed, s_rel, s_ch, cb)
+
+
+def quantize_weight_noalloc(w: torch.Tensor, seed: int = 0, out: QuantizedLinear | None = None) -> QuantizedLinear:
+    """quantize_weight without a workspace: the library's static scratch serves instead, so the
+    library call allocates nothing (the outputs here are allocated unless `out` is given)."""
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    wp = _dev(w, "w", (torch.float32, torch.bfloat16))
+    dev = w.device
+    if out is None:
+        out = QuantizedLinear(torch.empty((n, k // 2), dtype=torch.int8, device=dev),
+                              torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                              torch.empty((n,), dtype=torch.float32, device=dev),
+                              torch.empty((16,), dtype=torch.float32, device=dev))
+    _, pp, sp, cp, bp = _layer_ptrs(out, k, dev, "out")
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_quantize_weight_noalloc(wp, _fdtype(w), n, k, seed & (2**64 - 1), pp, sp, cp, bp,
+                                                  _stream()), "w4a8_quantize_weight_noalloc")
+    return out
 
 
 def prepare_activation(x: torch.Tensor, out=None):

@@ -103,6 +103,26 @@ int w4a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, uint6
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 
+int w4a8_quantize_weight_noalloc(const void *w, int w_dtype, int64_t N, int64_t K, uint64_t seed,
+                                 int8_t *packed, uint8_t *s_rel, float *s_channel, float *codebook,
+                                 void *stream) {
+    if (!w || !packed || !s_rel || !s_channel || !codebook) return W4A8_ERR_NULL;
+    if (N < 1 || !valid_k(K) || N > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
+    if (!valid_dtype(w_dtype)) return W4A8_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(s_rel) || !aligned16(s_channel) ||
+        !aligned16(codebook))
+        return W4A8_ERR_ALIGN;
+    int st = current_device(nullptr);
+    if (st != W4A8_OK) return st;
+    void *ws = nullptr;
+    size_t cap = 0;
+    if (w4a8::quantize_scratch(&ws, &cap) != hipSuccess) return W4A8_ERR_HIP;
+    if (w4a8::quantize_workspace_bytes(N, K) > cap) return W4A8_ERR_WORKSPACE;
+    hipError_t e = w4a8::launch_quantize(w, w_dtype == W4A8_BF16, N, K, seed, packed, s_rel, s_channel,
+                                         codebook, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
 int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *x_q,
                             float *s_x, void *stream) {
     if (!x || !x_q || !s_x) return W4A8_ERR_NULL;

@@ -27,6 +27,8 @@
 //  6. k_assign_pack: per row, rotate and normalise again (the arithmetic of steps 1 and 2),
 //     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 }, two indices per
 //     byte, even element in the low nibble.
+#include <atomic>
+
 #include "w4a8_internal.h"
 
 namespace w4a8 {
@@ -66,6 +68,10 @@ WsLayout layout(int64_t N, int64_t K) {
     const int64_t NK = N * K;
     return layout_for_sample(NK < kSampleMax ? NK : kSampleMax);
 }
+
+// The largest workspace any shape needs (a full 2^20-value sample): the size of the
+// no-allocation entry point's static scratch.
+constexpr size_t kScratchBytes = layout_for_sample(kSampleMax).total;
 
 // The group-scale code of one 16-group spread over 4 lanes (rotated values v, row max rmax).
 __device__ __forceinline__ uint32_t group_code(const float v[4], float rmax) {
@@ -331,9 +337,36 @@ __global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict
     }
 }
 
+// Scratch of the no-allocation entry point: one array per device, as large as the largest
+// workspace (12,583,168 bytes), held by every device the library runs on until the process
+// ends.  In host code its name stands for the host-side shadow only; kernels get the device
+// address that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+
 }  // namespace
 
 size_t quantize_workspace_bytes(int64_t N, int64_t K) { return layout(N, K).total; }
+
+hipError_t quantize_scratch(void **ptr, size_t *bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // with this device current: its own copy of the array (two threads may both look it
+        // up; they store the same address)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    *bytes = kScratchBytes;
+    return hipSuccess;
+}
 
 hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint64_t seed,
                            int8_t *packed, uint8_t *s_rel, float *s_ch, float *cb,

@@ -323,6 +323,9 @@ hipError_t launch_w8_gemv(const W8Args &a, int num_cu, hipStream_t stream);
 hipError_t launch_w8_gemm(const W8Args &a, hipStream_t stream);
 
 size_t quantize_workspace_bytes(int64_t N, int64_t K);
+// The no-allocation entry point's scratch on the current device: its device address and
+// size (the first call on a device looks the address up).
+hipError_t quantize_scratch(void **ptr, size_t *bytes);
 hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint64_t seed,
                            int8_t *packed, uint8_t *s_rel, float *s_ch, float *cb,
                            void *workspace, hipStream_t stream);
