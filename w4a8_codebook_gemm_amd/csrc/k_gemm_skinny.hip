@@ -22,7 +22,10 @@
 //    L2 resident) and converts the int8 values to fp16 exactly with a byte permute and a
 //    packed-fp16 subtract (bias 1152: bytes b + 128 under an fp16 exponent of 1024).
 //    Tokens past M and rows past N read zero through the buffer bounds.
-//  * A workgroup owns NT consecutive 16-row tiles; its waves (4 to 16, as registers allow)
+//  * One workgroup per compute unit: each owns ceil(N / CUs) consecutive rows as NT 16-row
+//    tiles, the last one partial (its rows past the workgroup's range read zero through the
+//    buffer bounds and are never stored), so every CU streams an equal share; its waves (4 to
+//    16, as registers allow)
 //    split K (wave w takes every W-th 128-k half-block, so the waves stream adjacent pieces
 //    of the same rows together) and each keeps its NT x MT16 accumulator tiles in registers.
 //    Each wave's next half-block is in flight while it computes one (a ring of two; a third
@@ -32,10 +35,10 @@
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
 //    Up to 48 tokens the table reads of the next row tile are issued before the current
 //    tile's multiplies and MFMAs (scheduling barriers keep that order).
-//  * Start-up: the codebook and the workgroup's group scales are requested before the first
-//    weight loads (a request behind them waits for them to drain from HBM); the scales go
-//    straight to LDS through the buffer unit (16 B per lane), so the weight stream carries
-//    no 2-byte loads.
+//  * Start-up: the workgroup's group scales are requested before the first weight loads (a
+//    request behind them waits for them to drain from HBM); they go straight to LDS through
+//    the buffer unit (16 B per lane), so the weight stream carries no 2-byte loads.  The
+//    codebook comes through the scalar cache, outside the in-order vector load counter.
 #include <type_traits>
 
 #include <atomic>
@@ -85,7 +88,7 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
 }
 
 template <int NT, int MT16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
+__global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg) {
     static_assert(WAVES * NT <= kSmemBytes / 1024, "reduction buffer");
     // pair table (later the wave reduction), then the staged group scales
     extern __shared__ __align__(16) char smem[];
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t r_begin = (int64_t)blockIdx.x * NT * 16;
-    const int nrows = (int)min((int64_t)NT * 16, N - r_begin);
+    const int64_t r_begin = (int64_t)blockIdx.x * rows_wg;
+    const int nrows = (int)min((int64_t)rows_wg, N - r_begin);
     const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
 
     const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
@@ -104,17 +107,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.x_q, (short)0, (int)(M * K), 0x00020000);
 
-    // the codebook (four 16-byte loads of one line), then the group scales of the
-    // workgroup's rows (nrows x K/16 contiguous bytes) copied to LDS 1 KiB per wave
-    // instruction, all before the first weight load
-    const __amdgpu_buffer_rsrc_t rs_cb = __builtin_amdgcn_make_buffer_rsrc((void *)a.cb, (short)0, kLevels * 4, 0x00020000);
+    // the codebook (scalar loads), then the group scales of the workgroup's rows (nrows x
+    // K/16 contiguous bytes) copied to LDS 1 KiB per wave instruction, all before the first
+    // weight load
+    const __attribute__((address_space(4))) float *cbk = (const __attribute__((address_space(4))) float *)a.cb;
     float cbv[kLevels];
 #pragma unroll
-    for (int q = 0; q < kLevels / 4; q++) {
-        const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs_cb, 16 * q, 0, 0);
-        cbv[4 * q] = __uint_as_float(c.x); cbv[4 * q + 1] = __uint_as_float(c.y);
-        cbv[4 * q + 2] = __uint_as_float(c.z); cbv[4 * q + 3] = __uint_as_float(c.w);
-    }
+    for (int q = 0; q < kLevels; q++) cbv[q] = cbk[q];
     const int nsc = (int)(nrows * grpbytes / 16);
     for (int blk = 64 * wave; blk < nsc; blk += 64 * WAVES)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (__attribute__((address_space(3))) void *)(ss + 16 * blk), 16,
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         const int64_t r = r_begin + 16 * t + i;
-        rsc[t] = r < N ? a.s_ch[r] * scale : 0.0f;
+        rsc[t] = r < r_begin + nrows ? a.s_ch[r] * scale : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < MT16; u++) {
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a) {
                 float v = 0.0f;
 #pragma unroll
                 for (int w = 0; w < WAVES; w++) v += red[(w * NT + t) * 64 + src][comp];
-                if (r < N) {
+                if (r < r_begin + nrows) {
                     const float val = (v * rsc[t]) * sxm;
                     if (a.y_bf16)
                         static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(val);
@@ -317,9 +316,9 @@ template <int NT, int MT16>
 constexpr int waves_for() { return (MT16 == 1 && NT <= 3) ? 16 : (MT16 <= 2 ? 8 : 4); }
 
 template <int NT, int MT16>
-hipError_t launch_one(const LinearArgs &a, unsigned grid, hipStream_t stream) {
+hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
-    const int64_t lds = kSmemBytes + skinny_scale_bytes(16 * NT, a.K / kGroup);
+    const int64_t lds = kSmemBytes + skinny_scale_bytes(rows_wg, a.K / kGroup);
     // set once per kernel instance; concurrent first calls may both set it, which is harmless
     static std::atomic<bool> attr_set{false};
     if (!attr_set.load(std::memory_order_acquire)) {
@@ -328,17 +327,17 @@ hipError_t launch_one(const LinearArgs &a, unsigned grid, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set.store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a);
+    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a, rows_wg);
     return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_nt(const LinearArgs &a, unsigned grid, hipStream_t stream) {
+hipError_t launch_nt(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
     switch ((a.M + 15) / 16) {
-        case 1: return launch_one<NT, 1>(a, grid, stream);
-        case 2: return launch_one<NT, 2>(a, grid, stream);
-        case 3: return launch_one<NT, 3>(a, grid, stream);
-        case 4: return launch_one<NT, 4>(a, grid, stream);
+        case 1: return launch_one<NT, 1>(a, grid, rows_wg, stream);
+        case 2: return launch_one<NT, 2>(a, grid, rows_wg, stream);
+        case 3: return launch_one<NT, 3>(a, grid, rows_wg, stream);
+        case 4: return launch_one<NT, 4>(a, grid, rows_wg, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -355,20 +354,20 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
     if (!skinny_supported(a.M, a.N, a.K)) return hipErrorInvalidValue;
-    // tiles per workgroup: enough to give every CU one workgroup, at most kMaxTiles
-    const int64_t tiles = (a.N + 15) / 16;
-    // (fewer for long rows: the staged scales of a workgroup's rows must fit in LDS)
-    int64_t nt = (tiles + num_cu - 1) / num_cu;
-    if (nt > kMaxTiles) nt = kMaxTiles;
-    while (nt > 1 && kSmemBytes + skinny_scale_bytes(16 * nt, a.K / kGroup) > kSkinnyLdsMax) nt--;
-    if (nt < 1) nt = 1;
-    const unsigned grid = (unsigned)((tiles + nt - 1) / nt);
+    // rows per workgroup: an equal share for every CU, at most kMaxTiles tiles (and fewer
+    // for long rows: the staged scales of a workgroup's rows must fit in LDS)
+    int64_t rows = (a.N + num_cu - 1) / num_cu;
+    if (rows > 16 * kMaxTiles) rows = 16 * kMaxTiles;
+    while (rows > 16 && kSmemBytes + skinny_scale_bytes(rows, a.K / kGroup) > kSkinnyLdsMax) rows -= 16;
+    if (rows < 1) rows = 1;
+    const int64_t nt = (rows + 15) / 16;
+    const unsigned grid = (unsigned)((a.N + rows - 1) / rows);
     switch (nt) {
-        case 1: return launch_nt<1>(a, grid, stream);
-        case 2: return launch_nt<2>(a, grid, stream);
-        case 3: return launch_nt<3>(a, grid, stream);
-        case 4: return launch_nt<4>(a, grid, stream);
-        default: return launch_nt<5>(a, grid, stream);
+        case 1: return launch_nt<1>(a, grid, (int)rows, stream);
+        case 2: return launch_nt<2>(a, grid, (int)rows, stream);
+        case 3: return launch_nt<3>(a, grid, (int)rows, stream);
+        case 4: return launch_nt<4>(a, grid, (int)rows, stream);
+        default: return launch_nt<5>(a, grid, (int)rows, stream);
     }
 }
 
