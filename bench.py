@@ -166,6 +166,9 @@ def probes():
     lib.bench_read_launch.restype = ctypes.c_int
     lib.bench_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.bench_valu_launch.restype = ctypes.c_int
+    lib.bench_stream_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.bench_stream_launch.restype = ctypes.c_int
     return lib
 
 
@@ -204,6 +207,44 @@ def read_ceiling(torch, nbytes, copies=COPIES):
                                                   us_per_launch=round(t * 1e6, 3))
                 del g
     del bufs
+    torch.cuda.empty_cache()
+    return best, cfg
+
+
+def stream_ceiling(torch, in_bytes, copies=COPIES):
+    """The achievable rate of a streaming read + write in the activation preparation's
+    proportion (4 bytes read per byte written, fp32 in and int8 out) at in_bytes read per
+    launch, over `copies` distinct inputs, timed like the kernels: the best over one, two or
+    four workgroups per compute unit, 256 / 512 / 1024 threads and 1 / 2 / 4 loads in flight
+    per thread.  Returns (GB/s of read + written bytes, config) or None when the helper is not
+    built."""
+    lib = probes()
+    if lib is None:
+        return None
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = in_bytes // 16 * 16
+    srcs = [torch.full((n,), c + 1, dtype=torch.uint8, device="cuda") for c in range(copies)]
+    dst = torch.empty((n // 4,), dtype=torch.uint8, device="cuda")
+    best, cfg = 0.0, None
+    for per_cu in (1, 2, 4):
+        for threads in (256, 512, 1024):
+            for depth in (1, 2, 4):
+                blocks = per_cu * cus
+
+                def launch():
+                    st = torch.cuda.current_stream().cuda_stream
+                    for b in srcs:
+                        rc = lib.bench_stream_launch(b.data_ptr(), n, dst.data_ptr(), blocks, threads, depth, st)
+                        if rc != 0:
+                            raise RuntimeError(f"bench_stream_launch: HIP error {rc}")
+                g = make_graph(torch, launch)
+                t = time_kernel_graph(torch, g) / copies
+                rate = (n + n // 4) / t / 1e9
+                if rate > best:
+                    best, cfg = rate, dict(workgroups_per_cu=per_cu, threads=threads, loads_in_flight_per_thread=depth,
+                                           us_per_launch=round(t * 1e6, 3))
+                del g
+    del srcs, dst
     torch.cuda.empty_cache()
     return best, cfg
 
@@ -573,12 +614,19 @@ def prepare_rate(w, torch, S, M, ks=(5120, 17408)):
         g = make_graph(torch, lambda: [w.prepare_activation(x, out=(x_q, s_x)) for x in xs])
         t = time_kernel_graph(torch, g) / COPIES
         byt = prepare_bytes(M, k)
-        res[f"{M}x{k}"] = dict(kernel="k_prepare (fp32 x)", us=round(t * 1e6, 2), per_launch_bytes=byt,
-                               roofline=dict(bound="hbm", achieved=round(byt / t / 1e9, 1), peak=HBM_PEAK_GBS,
-                                             unit="GB/s", frac=round(byt / t / 1e9 / HBM_PEAK_GBS, 4)))
-        log(f"prepare M={M} K={k}: {t * 1e6:.2f} us, {byt / t / 1e9:.1f} GB/s")
         del xs, g
         torch.cuda.empty_cache()
+        line = dict(kernel="k_prepare_tokens (fp32 x)", us=round(t * 1e6, 2), per_launch_bytes=byt,
+                    roofline=dict(bound="hbm", achieved=round(byt / t / 1e9, 1), peak=HBM_PEAK_GBS,
+                                  unit="GB/s", frac=round(byt / t / 1e9 / HBM_PEAK_GBS, 4)))
+        sc = stream_ceiling(torch, M * k * 4)
+        if sc is not None:
+            line["roofline"]["stream_ceiling_gbs"] = round(sc[0], 1)
+            line["roofline"]["stream_ceiling_config"] = sc[1]
+            line["roofline"]["frac_of_stream_ceiling"] = round(byt / t / 1e9 / sc[0], 4)
+        res[f"{M}x{k}"] = line
+        log(f"prepare M={M} K={k}: {t * 1e6:.2f} us, {byt / t / 1e9:.1f} GB/s"
+            + (f"; streaming read + write ceiling {sc[0]:.1f} GB/s ({sc[1]})" if sc else ""))
     return res
 
 

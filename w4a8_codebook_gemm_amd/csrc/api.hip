@@ -129,9 +129,10 @@ int w4a8_prepare_activation(const void *x, int x_dtype, int64_t M, int64_t K, in
     if (M < 1 || !valid_k(K) || M > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
     if (!valid_dtype(x_dtype)) return W4A8_ERR_DTYPE;
     if (!aligned16(x) || !aligned16(x_q) || !aligned16(s_x)) return W4A8_ERR_ALIGN;
-    int st = current_device(nullptr);
+    int num_cu = 0;
+    int st = current_device(&num_cu);
     if (st != W4A8_OK) return st;
-    hipError_t e = w4a8::launch_prepare(x, x_dtype == W4A8_BF16, M, K, x_q, s_x,
+    hipError_t e = w4a8::launch_prepare(x, x_dtype == W4A8_BF16, M, K, x_q, s_x, num_cu,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
@@ -261,10 +262,11 @@ int w4a8_w8a8_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, 
     if (N < 1 || !valid_k(K) || K > w4a8::kW8MaxK || N > (int64_t(1) << 31) - 1) return W4A8_ERR_SHAPE;
     if (!valid_dtype(w_dtype)) return W4A8_ERR_DTYPE;
     if (!aligned16(w) || !aligned16(w_q) || !aligned16(s_w)) return W4A8_ERR_ALIGN;
-    int st = current_device(nullptr);
+    int num_cu = 0;
+    int st = current_device(&num_cu);
     if (st != W4A8_OK) return st;
     // a weight row is quantised exactly as a token is: rotate, per-row max / 127, round
-    hipError_t e = w4a8::launch_prepare(w, w_dtype == W4A8_BF16, N, K, w_q, s_w,
+    hipError_t e = w4a8::launch_prepare(w, w_dtype == W4A8_BF16, N, K, w_q, s_w, num_cu,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }

@@ -259,7 +259,7 @@ __device__ __forceinline__ uint2 decode8(const CbI8 &c, uint32_t w) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Shapes were validated by the caller.
 hipError_t launch_prepare(const void *x, int x_bf16, int64_t M, int64_t K, int8_t *x_q,
-                          float *s_x, hipStream_t stream);
+                          float *s_x, int num_cu, hipStream_t stream);
 
 struct LinearArgs {
     const int8_t *x_q;
