@@ -43,11 +43,26 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 192, BK = 64;
-constexpr int kThreads = 512;
-constexpr int JB = BN / 64;                    // 32-row weight fragments per wave
+constexpr int BK = 64;
 constexpr int kPitch = BK + 8;                 // fp16 per LDS row (144 B)
-constexpr int kXStage = BM * kPitch, kBStage = BN * kPitch;
+
+// Tile configurations: BM tokens x BN weight rows per workgroup, WM x WN waves, each wave
+// (BM / WM) x (BN / WN) as 32 x 32 fragments.  Every configuration accumulates each output
+// over the same k order with the same MFMA, so they give identical results; the prefill one
+// (256 x 192, 8 waves) suits many tokens, the small ones give a few dozen tokens enough
+// workgroups for every CU.
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int IB = BM / WM / 32, JB = BN / WN / 32;   // 32 x 32 fragments per wave
+    static constexpr int kXStage = BM * kPitch, kBStage = BN * kPitch;
+    static_assert(IB >= 1 && JB >= 1 && BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "tile");
+    static_assert(2 * BM <= kThreads && 2 * BN <= kThreads && (2 * BN) % 64 == 0, "staging roles");
+};
+using CfgPrefill = Cfg<256, 192, 4, 2>;
+using CfgSmall = Cfg<64, 64, 2, 2>;
+using CfgTiny = Cfg<32, 64, 1, 2>;
 
 // four int8 -> four fp16 (exact): bytes b ^ 0x80 under the fp16 exponent of 1024 give
 // 1024 + b + 128; subtracting 1152 leaves b
@@ -68,13 +83,16 @@ struct Stage {
 template <int J>
 using IC = std::integral_constant<int, J>;
 
-__global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m, int tiles) {
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tiles_m, int tiles) {
+    constexpr int BM = C::BM, BN = C::BN, IB = C::IB, JB = C::JB;
+    constexpr int kXStage = C::kXStage, kBStage = C::kBStage;
     __shared__ __align__(16) _Float16 xs[2][kXStage];
     __shared__ __align__(16) _Float16 bs[2][kBStage];
     __shared__ uint32_t tab[256];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t M = a.M, N = a.N, K = a.K;
 
     // consecutive workgroups go to consecutive XCDs: XCD x takes the contiguous tile run
@@ -89,17 +107,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
     for (int j = 0; j < kLevels; j++) cmax = fmaxf(cmax, fabsf(a.cb[j]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
-    if (tid < 256) {
-        const float inv = ldexpf(1.0f, -ex);
-        tab[tid] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[tid & 15] * inv)) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[tid >> 4] * inv)) << 16);
-    }
+    const float inv = ldexpf(1.0f, -ex);
+    for (int e = tid; e < 256; e += C::kThreads)   // fewer than 256 threads: several entries each
+        tab[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e & 15] * inv)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e >> 4] * inv)) << 16);
 
     // ---- staging roles: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight row pr,
     // weights [32 ph, 32 ph + 32) (two groups).  Rows past M or N re-read the last valid row:
     // they feed only outputs that are never stored.  Threads past 2 BN load like the last
-    // row's but decode nothing.
-    const int xr = tid >> 1, xh = tid & 1;
+    // row's but decode nothing; threads past 2 BM load like the last token's and stage
+    // nothing.
+    const bool xdec = (tid >> 1) < BM;             // wave-uniform: 2 BM is a multiple of 64
+    const int xr = xdec ? tid >> 1 : BM - 1, xh = tid & 1;
     const int pr0 = tid >> 1, ph = tid & 1;
     const bool pdec = pr0 < BN;                    // wave-uniform: 2 BN is a multiple of 64
     const int pr = pdec ? pr0 : BN - 1;
@@ -126,11 +145,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
     auto lstore = [&](auto bufc, const Stage &st) {
         constexpr int buf = decltype(bufc)::value;
         const uint32_t xw[8] = {st.x0.x, st.x0.y, st.x0.z, st.x0.w, st.x1.x, st.x1.y, st.x1.z, st.x1.w};
-        uint4 *dx = reinterpret_cast<uint4 *>(xdst + buf * kXStage);
+        if (xdec) {
+            uint4 *dx = reinterpret_cast<uint4 *>(xdst + buf * kXStage);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint2 c0 = i8x4_to_f16x4(xw[2 * i]), c1 = i8x4_to_f16x4(xw[2 * i + 1]);
-            dx[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+            for (int i = 0; i < 4; i++) {
+                const uint2 c0 = i8x4_to_f16x4(xw[2 * i]), c1 = i8x4_to_f16x4(xw[2 * i + 1]);
+                dx[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+            }
         }
         if (pdec) {
             const uint32_t sv = st.s >> sshift;
@@ -150,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
         }
     };
 
-    float16_t acc[2][JB];
+    float16_t acc[IB][JB];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < IB; i++)
 #pragma unroll
         for (int j = 0; j < JB; j++)
 #pragma unroll
@@ -168,22 +189,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
     __syncthreads();
 
     const int half = lane >> 5, l32 = lane & 31;
-    const _Float16 *const xrd = &xs[0][(wm * 64 + l32) * kPitch + 8 * half];
-    const _Float16 *const brd = &bs[0][(wn * (BN / 2) + l32) * kPitch + 8 * half];
+    const _Float16 *const xrd = &xs[0][(wm * (BM / C::WM) + l32) * kPitch + 8 * half];
+    const _Float16 *const brd = &bs[0][(wn * (BN / C::WN) + l32) * kPitch + 8 * half];
 
     auto mfmas = [&](auto bufc) {
         constexpr int buf = decltype(bufc)::value;
 #pragma unroll
         for (int g = 0; g < BK / 16; g++) {
-            half8_t A[2], B[JB];
+            half8_t A[IB], B[JB];
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++)
+            for (int ib = 0; ib < IB; ib++)
                 A[ib] = *reinterpret_cast<const half8_t *>(xrd + buf * kXStage + ib * 32 * kPitch + g * 16);
 #pragma unroll
             for (int jb = 0; jb < JB; jb++)
                 B[jb] = *reinterpret_cast<const half8_t *>(brd + buf * kBStage + jb * 32 * kPitch + g * 16);
 #pragma unroll
-            for (int ib = 0; ib < 2; ib++)
+            for (int ib = 0; ib < IB; ib++)
 #pragma unroll
                 for (int jb = 0; jb < JB; jb++)
                     acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[ib], B[jb], acc[ib][jb], 0, 0, 0);
@@ -210,14 +231,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
     const float scale = ldexpf(1.0f, ex - 7);
 #pragma unroll
     for (int jb = 0; jb < JB; jb++) {
-        const int64_t r = n0 + wn * (BN / 2) + jb * 32 + l32;
+        const int64_t r = n0 + wn * (BN / C::WN) + jb * 32 + l32;
         if (r >= N) continue;
         const float rsc = a.s_ch[r] * scale;
 #pragma unroll
-        for (int ib = 0; ib < 2; ib++)
+        for (int ib = 0; ib < IB; ib++)
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int64_t m = m0 + wm * 64 + ib * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                const int64_t m = m0 + wm * (BM / C::WM) + ib * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
                 if (m < M) {
                     const float val = (acc[ib][jb][v] * rsc) * a.s_x[m];
                     if (a.y_bf16)
@@ -229,13 +250,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_f16(LinearArgs a, int tiles_m
     }
 }
 
-}  // namespace
-
-hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream) {
-    const int64_t tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    hipLaunchKernelGGL(k_gemm_f16, dim3((unsigned)(tm * tn)), dim3(kThreads), 0, stream, a, (int)tm,
+template <class C>
+hipError_t launch_cfg(const LinearArgs &a, hipStream_t stream) {
+    const int64_t tm = (a.M + C::BM - 1) / C::BM, tn = (a.N + C::BN - 1) / C::BN;
+    hipLaunchKernelGGL(k_gemm_f16<C>, dim3((unsigned)(tm * tn)), dim3(C::kThreads), 0, stream, a, (int)tm,
                        (int)(tm * tn));
     return hipGetLastError();
+}
+
+}  // namespace
+
+// The tile configuration by token count: the results do not depend on it.
+hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream) {
+    if (a.M <= CfgTiny::BM) return launch_cfg<CfgTiny>(a, stream);
+    if (a.M <= CfgSmall::BM) return launch_cfg<CfgSmall>(a, stream);
+    return launch_cfg<CfgPrefill>(a, stream);
+}
+
+bool gemm_f16_tiles_fit(int64_t M, int64_t N) {
+    const int64_t bm = M <= CfgTiny::BM ? CfgTiny::BM : (M <= CfgSmall::BM ? CfgSmall::BM : CfgPrefill::BM);
+    const int64_t bn = M <= CfgSmall::BM ? CfgSmall::BN : CfgPrefill::BN;
+    return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) <= (int64_t(1) << 31) - 1;
 }
 
 }  // namespace w4a8
