@@ -25,7 +25,8 @@ matrices) / measured time per step.  The same line carries:
   model         62 decoder layers x 8 projections (13.9 GB resident, 496 allocations), one
                 token = one fused multi-layer call per input (248 launches) from one HIP graph,
                 and the same token with one launch per projection (496);
-  prefill       M=2048 GEMMs on both MLP shapes: int8-MFMA (per-16 fold) and f16-MFMA;
+  prefill       M=2048 GEMMs on both MLP shapes: the int8-codebook and fp16-codebook routes
+                (f16 MFMA on decoded weights) and the requantised route (int8 MFMA);
   w8a8          the INT8 ConvRot comparator (same rotation and int8 activations, per-row
                 int8 weights): decode GEMV on both MLP shapes (prepared x_q), a decode step
                 with its prepare launches beside the W4A8 unfused step, and M=2048 GEMMs;
@@ -59,18 +60,6 @@ INT8_PEAK_TOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
 
 
-def fold_ceiling_tops(valu_lane_ops):
-    """What the exact per-16 fold allows, from the measured vector-ALU rate of its two
-    instructions (v_cvt_f32_i32 + v_fmac_f32 per int32 group partial, lane operations per
-    second at the int8 kernel's two waves per SIMD; packed fp32 is off and the conversion has
-    no packed form).  Per multiply-accumulate the fold costs 2 / 16 lane operations:
-    T_valu = (1 / 8) / R.  The MFMA that covers one group of 16 (v_mfma_i32_32x32x16_i8) runs
-    at half the int8 peak: T_mfma = 2 / (peak / 2).  Returns (overlapped, serial) TOP/s:
-    2 / max(T_valu, T_mfma) if the two units run side by side from different waves (the upper
-    bound), 2 / (T_valu + T_mfma) if they take turns; neither depends on M, N or K."""
-    t_valu = (1.0 / 8.0) / valu_lane_ops
-    t_mfma = 2.0 / (INT8_PEAK_TOPS * 1e12 / 2.0)
-    return 2.0 / max(t_valu, t_mfma) / 1e12, 2.0 / (t_valu + t_mfma) / 1e12
 COPIES = 8
 METRIC = "W4A8 linear: effective weight GB/s (M=1) + int8 TOPS (M=2048) on 1 MI355X"
 SWEEP_M = (1, 2, 4, 8, 16, 32, 64)
@@ -164,8 +153,6 @@ def probes():
     lib.bench_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.bench_read_launch.restype = ctypes.c_int
-    lib.bench_valu_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.bench_valu_launch.restype = ctypes.c_int
     lib.bench_stream_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.bench_stream_launch.restype = ctypes.c_int
@@ -247,27 +234,6 @@ def stream_ceiling(torch, in_bytes, copies=COPIES):
     del srcs, dst
     torch.cuda.empty_cache()
     return best, cfg
-
-
-def valu_rate(torch, iters=4096):
-    """Lane operations per second of the int8 fold's instruction pair (v_cvt_f32_i32 +
-    v_fmac_f32, 16 independent accumulators per thread) with one 512-thread workgroup per
-    compute unit, i.e. two waves per SIMD (the helper kernel of bench_probes.hip)."""
-    lib = probes()
-    if lib is None:
-        return None
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.zeros(cus * 512, dtype=torch.float32, device="cuda")
-
-    def launch():
-        st = torch.cuda.current_stream().cuda_stream
-        for _ in range(4):
-            rc = lib.bench_valu_launch(cus, iters, sink.data_ptr(), st)
-            if rc != 0:
-                raise RuntimeError(f"bench_valu_launch: HIP error {rc}")
-    g = make_graph(torch, launch)
-    t = time_kernel_graph(torch, g) / 4
-    return cus * 512 * iters * 32 / t
 
 
 def busy(torch):
@@ -579,19 +545,14 @@ def prefill(w, torch, S, shapes, M=2048):
             pre[f"{n}x{k}/{name}"] = dict(algo=name, us=round(t * 1e6, 1), tops=round(tops, 1))
             log(f"prefill {name} M={M} {n}x{k}: {t * 1e6:.1f} us, {tops:.1f} TOPS")
     summary = {}
-    for name, peak, unit in (("mfma_i8", INT8_PEAK_TOPS, "TOP/s"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s"),
-                             ("mfma_rq", INT8_PEAK_TOPS, "TOP/s")):
+    # each route against the peak of the matrix-core instruction it runs: the two
+    # decoded-weight routes on v_mfma_f32_32x32x16_f16 (the int8 route's int8 x int8 products
+    # are exact there), the requantised route on v_mfma_i32_32x32x32_i8
+    for name, peak, unit, inst in (("mfma_i8", F16_PEAK_TFLOPS, "TOP/s", "f16"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s", "f16"),
+                                   ("mfma_rq", INT8_PEAK_TOPS, "TOP/s", "i8")):
         mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
-        summary[name] = dict(tops=round(mean, 1), roofline=dict(
+        summary[name] = dict(tops=round(mean, 1), mfma=inst, roofline=dict(
             bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
-    r = valu_rate(torch)
-    if r:
-        fc, fs = fold_ceiling_tops(r)
-        summary["mfma_i8"]["fold_ceiling"] = dict(
-            valu_lane_ops_per_s=round(r / 1e12, 2), unit="TOP/s", tops=round(fc, 1), serial_tops=round(fs, 1),
-            frac=round(summary["mfma_i8"]["tops"] / fc, 4), frac_of_serial=round(summary["mfma_i8"]["tops"] / fs, 4))
-        log(f"fold instruction pair at two waves per SIMD: {r / 1e12:.2f} T lane operations/s; fold ceiling "
-            f"{fc:.0f} TOP/s overlapped with the MFMA, {fs:.0f} TOP/s taking turns")
     del pl
     torch.cuda.empty_cache()
     return dict(tokens=M, ops_per_gemm="2*M*N*K", shapes=pre, prepare=prepare_rate(w, torch, S, M), **summary)

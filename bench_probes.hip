@@ -11,13 +11,8 @@
 //    preparation's proportion, four bytes read per byte written (fp32 in, int8 out).  Each
 //    workgroup converts a contiguous share: a 16-byte load per thread and step (DEPTH steps
 //    in flight), a 4-byte store of its low bytes.
-//  * bench_valu_launch: the vector-ALU rate of the int8 route's group fold, one
-//    v_cvt_f32_i32 and one v_fmac_f32 per int32 partial, on 16 independent accumulators per
-//    thread (the 16 outputs one lane holds of a 32 x 32 MFMA tile), with one 512-thread
-//    workgroup per compute unit: two waves per SIMD, the occupancy of the int8 prefill
-//    kernel.  The LDS request keeps a second workgroup off each unit.
 //
-// All take device pointers, launch on the given stream and return the HIP error code of
+// Both take device pointers, launch on the given stream and return the HIP error code of
 // the launch.
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -85,35 +80,6 @@ int launch_stream(const void *src, uint64_t bytes, void *dst, int blocks, hipStr
     return (int)hipGetLastError();
 }
 
-constexpr int kValuThreads = 512;
-constexpr int kValuChains = 16;
-
-__global__ __launch_bounds__(kValuThreads) void k_valu(int iters, float s, float *sink) {
-    extern __shared__ float pad[];  // sized by the launch to keep one workgroup per unit
-    int p[kValuChains];
-    float acc[kValuChains];
-#pragma unroll
-    for (int c = 0; c < kValuChains; c++) {
-        p[c] = (int)(threadIdx.x * 31 + c);
-        acc[c] = 0.0f;
-    }
-    for (int it = 0; it < iters; it++) {
-        // an empty statement that claims to change the partials keeps each conversion in the
-        // loop (it emits no instruction)
-#pragma unroll
-        for (int c = 0; c < kValuChains; c++) asm volatile("" : "+v"(p[c]));
-#pragma unroll
-        for (int c = 0; c < kValuChains; c++) acc[c] = fmaf(s, (float)p[c], acc[c]);
-    }
-    float t = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kValuChains; c++) t += acc[c];
-    if (t == 1234.5f) {
-        pad[threadIdx.x] = t;
-        sink[blockIdx.x * kValuThreads + threadIdx.x] = pad[threadIdx.x ^ 1];
-    }
-}
-
 }  // namespace
 
 // threads in {256, 512, 1024}, depth in {1, 2, 4, 8}; bytes a multiple of 16, and a
@@ -141,20 +107,4 @@ extern "C" int bench_stream_launch(const void *src, uint64_t bytes, void *dst, i
     W4A8_STREAM_CASE(1024, 1) W4A8_STREAM_CASE(1024, 2) W4A8_STREAM_CASE(1024, 4)
 #undef W4A8_STREAM_CASE
     return -1;
-}
-
-// blocks workgroups of 512 threads, each running `iters` rounds of 16 (convert, fma) pairs
-// per thread; sink holds blocks * 512 floats.  Lane operations per launch:
-// blocks * 512 * iters * 32.
-extern "C" int bench_valu_launch(int blocks, int iters, float *sink, void *stream) {
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_valu),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-        if (e != hipSuccess) return (int)e;
-        attr = true;
-    }
-    hipLaunchKernelGGL(k_valu, dim3((unsigned)blocks), dim3(kValuThreads), 96 * 1024,
-                       static_cast<hipStream_t>(stream), iters, 1.0f / 3.0f, sink);
-    return (int)hipGetLastError();
 }

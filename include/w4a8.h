@@ -71,11 +71,15 @@ typedef enum {
                                  into [0.5, 1) and rounded to fp16: a relative error of at most
                                  2^-11 per level (levels under 2^-14 of the largest: an absolute
                                  error of at most 2^-25 of that power of two), fp32 sums */
-    W4A8_ALGO_MFMA_I8 = 2,    /* int8 MFMA on the int8 form of the codebook, exact int32
-                                 per-16 partials, fp32 group-scale fold.  The int8 codebook is
-                                 cb_i8 = rint(codebook / s_cb), s_cb = max|codebook| / 127, so
-                                 each level moves by up to s_cb / 2: on top of the fp32 fold the
-                                 output carries up to s_x * s_channel * sum_g |dec(s_rel)| *
+    W4A8_ALGO_MFMA_I8 = 2,    /* the int8 form of the codebook, cb_i8 = rint(codebook / s_cb),
+                                 s_cb = max|codebook| / 127.  Each weight cb_i8[idx] * dec(s_rel)
+                                 is exact in fp16 (at most 11 significant bits, 2^-9 to 56896)
+                                 and each product with x_q exact in fp32, so a group's products
+                                 sum to its exact int8 partial times its group scale; f16 MFMA,
+                                 fp32 accumulation, y = acc * s_cb * s_channel * s_x (the same
+                                 tiles as MFMA_F16).  Each level moves by up to s_cb / 2: on top
+                                 of the fp32 accumulation the output carries up to
+                                 s_x * s_channel * sum_g |dec(s_rel)| *
                                  (s_cb / 2) * sum_{k in g} |x_q|.  That term is not inside the
                                  4e-3 bound of w4a8_linear for every input (activations that
                                  fall on small levels only can exceed it); dense activations
@@ -83,8 +87,9 @@ typedef enum {
                                  the automatic one */
     W4A8_ALGO_MFMA_F16 = 3,   /* f16 MFMA on decoded weights: fp16(codebook level x 2^-ex) times
                                  fp16(dec(s_rel) x 2^7) rounded to fp16 (at most 2^-10 relative
-                                 per weight), fp32 accumulation; 256 x 192 tiles, one workgroup
-                                 per tile (prefill) */
+                                 per weight), fp32 accumulation; one workgroup per tile of
+                                 256 tokens x 192 rows (64 x 64 up to 64 tokens, 32 x 64 up to
+                                 32) */
     W4A8_ALGO_MFMA_SKINNY = 4, /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
                                  16-row weight tiles streamed once, M*K < 2^31 */
     W4A8_ALGO_MFMA_RQ = 5     /* full-rate int8 MFMA on requantised weights (prefill):
@@ -194,8 +199,8 @@ W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t
  * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960), W4A8_ALGO_MFMA_SKINNY outside
  * its range (M <= 64, M*K < 2^31, 40*K < 2^31), W4A8_ALGO_MFMA_RQ for K > 131072 (the
  * int32 sum must stay exact), and the three prefill GEMMs (MFMA_I8, MFMA_F16, MFMA_RQ) for
- * more than 2^31 - 1 tiles of 256 tokens x 192 rows.  An unknown algorithm code returns
- * W4A8_ERR_DTYPE. */
+ * more than 2^31 - 1 workgroup tiles (see the algorithm list for the tile shapes).  An
+ * unknown algorithm code returns W4A8_ERR_DTYPE. */
 W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,

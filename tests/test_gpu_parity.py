@@ -3,8 +3,9 @@
 Integers -- packed indices, e4m3 group-scale bytes, row scales, codebook bits, int8
 activations and their scales -- must match bit for bit.  Products must satisfy
 |y - y_ref| <= 4e-3 * A with y_ref and A = sum_k |s_x x_q w_hat| from the oracle's fp64
-definition; the int8-MFMA path must also match the oracle's int8-codebook value y8 within
-the fp32 rounding of its fold, (G + 4) * 2^-24 * A8 for G = K/16 groups.  Full-size
+definition; the int8-codebook route must also match the oracle's int8-codebook value y8
+within (G + 4) * 2^-24 * A8 for G = K/16 groups (the fp32 rounding of one addition per group
+of 16 exact products, plus the epilogue's).  Full-size
 shapes are checked on sampled rows and tokens; small shapes span several tiles and ragged
 tails in full.
 """

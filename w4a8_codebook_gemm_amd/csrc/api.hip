@@ -155,11 +155,10 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
     if (algo == W4A8_ALGO_MFMA_SKINNY && !w4a8::skinny_supported(M, N, K)) return W4A8_ERR_SHAPE;
     if (algo == W4A8_ALGO_MFMA_RQ && !w4a8::gemm_rq_supported(M, N, K)) return W4A8_ERR_SHAPE;
-    // the prefill GEMMs launch one workgroup per tile (256 x 192, or smaller f16 tiles for
+    // the decoded-weight GEMMs launch one workgroup per tile (256 x 192, or smaller tiles for
     // few tokens)
-    if (algo == W4A8_ALGO_MFMA_I8 && ((M + 255) / 256) * ((N + 191) / 192) > (int64_t(1) << 31) - 1)
+    if ((algo == W4A8_ALGO_MFMA_I8 || algo == W4A8_ALGO_MFMA_F16) && !w4a8::gemm_dec_tiles_fit(M, N))
         return W4A8_ERR_SHAPE;
-    if (algo == W4A8_ALGO_MFMA_F16 && !w4a8::gemm_f16_tiles_fit(M, N)) return W4A8_ERR_SHAPE;
     int num_cu = 0;
     st = current_device(&num_cu);
     if (st != W4A8_OK) return st;

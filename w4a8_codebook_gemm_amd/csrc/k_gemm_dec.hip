@@ -1,23 +1,33 @@
-// Kernel 3b: prefill GEMM on f16 MFMA with the group scale folded into the decoded weight.
+// Kernel 3: prefill GEMM on f16 MFMA over weights decoded once per tile, with the per-16
+// group scale applied to each decoded weight.
 //
 // Model card "Qwen3.8-27B-uncensored-w4a8-convrot-ComfyUI", sections "Format" and "Why this
 // exists": 4-bit indices into a per-tensor 16-level codebook, an e4m3 scale per 16 values
-// and an fp32 scale per output row, executed on the GEMM path with a codebook
+// and an fp32 scale per output row, executed on the int8 GEMM path with a codebook
 // dequantisation step on top.
 //
-// Each weight is decoded once per tile to fp16 w16 = fp16(s16 * cb16[idx]) with
-// cb16 = fp16(cb / 2^ex) (max |cb| = f 2^ex, f in [0.5, 1)) and s16 = s_rel * 2^7 (exact:
-// an e4m3 value times a power of two; every finite e4m3 magnitude, 2^-9 to 448, lands in
-// [2^-2, 57344], so s16 and s16 * cb16 stay below the fp16 maximum 65504).  Two fp16
-// roundings give at most ~2^-10 relative error per weight, inside the layer's
-// 4e-3 * sum |x w| bound by construction; the 2^7 keeps products of small scales and
-// levels down to 2^-12 out of the fp16 subnormal range.  x_q is exact in fp16.  With the
-// group scale inside the weight, every group accumulates into the same fp32 MFMA
-// accumulator: no per-group fold on the vector ALU.
-//   y[m, r] = acc * 2^(ex - 7) * s_channel[r] * s_x[m].
+// Two forms of the codebook, one skeleton (template flag I8):
+//  * fp16 codebook (the automatic prefill route): w16 = fp16(s16 * cb16[idx]) with
+//    cb16 = fp16(cb / 2^ex) (max |cb| = f 2^ex, f in [0.5, 1)) and s16 = s_rel * 2^7 (exact:
+//    an e4m3 value times a power of two; every finite e4m3 magnitude, 2^-9 to 448, lands in
+//    [2^-2, 57344], so s16 and s16 * cb16 stay below the fp16 maximum 65504).  Two fp16
+//    roundings give at most ~2^-10 relative error per weight, inside the layer's
+//    4e-3 * sum |x w| bound by construction; the 2^7 keeps products of small scales and
+//    levels down to 2^-12 out of the fp16 subnormal range.
+//      y[m, r] = acc * 2^(ex - 7) * s_channel[r] * s_x[m].
+//  * int8 codebook (the int8 route): cb_i8 = rint(cb / s_cb), s_cb = max|cb| / 127, and
+//    w16 = cb_i8[idx] * s_rel, which fp16 holds exactly: |cb_i8| <= 127 (7 bits) times an
+//    e4m3 value (4 significant bits) has at most 11 significant bits, and the magnitudes run
+//    from 2^-9 to 127 * 448 = 56896, inside fp16's normal range.  Every product x_q * w16 is
+//    then exact in fp32 (8 + 11 bits), so each group's 16 products are exactly
+//    s_rel * sum x_q * cb_i8 -- the per-16 partial with its group scale folded in -- and the
+//    fp32 MFMA accumulation adds them up: the fold costs no vector-ALU work at all.
+//      y[m, r] = acc * s_cb * s_channel[r] * s_x[m].
+// x_q is exact in fp16.  With the group scale inside the weight, every group accumulates
+// into the same fp32 MFMA accumulator.
 //
-// Tile: 256 tokens x 192 weight rows per 512-thread workgroup, one workgroup per CU (the
-// 192-row tile divides both MLP shapes into nearly whole rounds of 256 tiles).  Waves
+// Tile (prefill): 256 tokens x 192 weight rows per 512-thread workgroup, one workgroup per
+// CU (the 192-row tile divides both MLP shapes into nearly whole rounds of 256 tiles).  Waves
 // 4 (tokens) x 2 (rows), each 64 x 96 = 2 x 3 fragments of v_mfma_f32_32x32x16_f16.  K
 // advances in stages of 64, double-buffered through LDS; the global loads run four stages
 // ahead in a ring of register stages, so a stage is decoded three steps after its loads
@@ -25,7 +35,7 @@
 //  * activations: int8 -> fp16 once per stage (exact, v_perm onto 0x6400 then one packed
 //    subtract) into [token][64 + 8 pad] rows;
 //  * weights: decoded once per stage by the whole workgroup -- a packed byte indexes a
-//    256-entry LDS table of fp16 pairs (cb16[low nibble], cb16[high nibble]), one packed
+//    256-entry LDS table of fp16 pairs (level[low nibble], level[high nibble]), one packed
 //    multiply applies the group scale -- into [row][64 + 8 pad] rows, so the MFMA loop
 //    reads plain fp16 fragments for both operands.
 // The 144-byte LDS rows put the 16 rows one 16-lane phase of a 16-byte fragment read
@@ -83,8 +93,8 @@ struct Stage {
 template <int J>
 using IC = std::integral_constant<int, J>;
 
-template <class C>
-__global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tiles_m, int tiles) {
+template <class C, bool I8>
+__global__ __launch_bounds__(C::kThreads) void k_gemm_dec(LinearArgs a, int tiles_m, int tiles) {
     constexpr int BM = C::BM, BN = C::BN, IB = C::IB, JB = C::JB;
     constexpr int kXStage = C::kXStage, kBStage = C::kBStage;
     __shared__ __align__(16) _Float16 xs[2][kXStage];
@@ -101,16 +111,21 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tile
     const int t = xcd * q + min(xcd, rem) + slot;
     const int64_t m0 = (int64_t)(t % tiles_m) * BM, n0 = (int64_t)(t / tiles_m) * BN;
 
-    // ---- codebook pair table: cb16 = fp16(cb / 2^ex); entry e = (cb16[e & 15], cb16[e >> 4])
+    // ---- codebook pair table, entry e = (level[e & 15], level[e >> 4]): cb16 = fp16(cb / 2^ex),
+    // or the integers cb_i8 = rint(cb / s_cb) (same fp32 arithmetic at every thread)
     float cmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < kLevels; j++) cmax = fmaxf(cmax, fabsf(a.cb[j]));
     int ex = 0;
     if (cmax > 0.0f) frexpf(cmax, &ex);
-    const float inv = ldexpf(1.0f, -ex);
+    const float s_cb = cmax / 127.0f;
+    auto level = [&](int j) {
+        if constexpr (I8) return (s_cb > 0.0f) ? rintf(a.cb[j] / s_cb) : 0.0f;
+        else return a.cb[j] * ldexpf(1.0f, -ex);
+    };
     for (int e = tid; e < 256; e += C::kThreads)   // fewer than 256 threads: several entries each
-        tab[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e & 15] * inv)) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(a.cb[e >> 4] * inv)) << 16);
+        tab[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)level(e & 15)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)level(e >> 4)) << 16);
 
     // ---- staging roles: token xr, bytes [32 xh, 32 xh + 32) of a stage; weight row pr,
     // weights [32 ph, 32 ph + 32) (two groups).  Rows past M or N re-read the last valid row:
@@ -155,8 +170,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tile
         }
         if (pdec) {
             const uint32_t sv = st.s >> sshift;
-            const _Float16 s0 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 0) * 128.0f);
-            const _Float16 s1 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 1) * 128.0f);
+            constexpr float kPre = I8 ? 1.0f : 128.0f;  // exact: a power of two
+            const _Float16 s0 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 0) * kPre);
+            const _Float16 s1 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 1) * kPre);
             const half2_t g0 = {s0, s0}, g1 = {s1, s1};
             const uint32_t pw[4] = {st.p.x, st.p.y, st.p.z, st.p.w};
             uint32_t o[16];
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tile
     }
 
     // ---- epilogue: lane holds column j = l32 (weight row), tokens 8(v/4) + 4 half + v%4
-    const float scale = ldexpf(1.0f, ex - 7);
+    const float scale = I8 ? s_cb : ldexpf(1.0f, ex - 7);
 #pragma unroll
     for (int jb = 0; jb < JB; jb++) {
         const int64_t r = n0 + wn * (BN / C::WN) + jb * 32 + l32;
@@ -250,24 +266,28 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_f16(LinearArgs a, int tile
     }
 }
 
-template <class C>
+template <class C, bool I8>
 hipError_t launch_cfg(const LinearArgs &a, hipStream_t stream) {
     const int64_t tm = (a.M + C::BM - 1) / C::BM, tn = (a.N + C::BN - 1) / C::BN;
-    hipLaunchKernelGGL(k_gemm_f16<C>, dim3((unsigned)(tm * tn)), dim3(C::kThreads), 0, stream, a, (int)tm,
+    hipLaunchKernelGGL((k_gemm_dec<C, I8>), dim3((unsigned)(tm * tn)), dim3(C::kThreads), 0, stream, a, (int)tm,
                        (int)(tm * tn));
     return hipGetLastError();
+}
+
+template <bool I8>
+hipError_t launch_form(const LinearArgs &a, hipStream_t stream) {
+    if (a.M <= CfgTiny::BM) return launch_cfg<CfgTiny, I8>(a, stream);
+    if (a.M <= CfgSmall::BM) return launch_cfg<CfgSmall, I8>(a, stream);
+    return launch_cfg<CfgPrefill, I8>(a, stream);
 }
 
 }  // namespace
 
 // The tile configuration by token count: the results do not depend on it.
-hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream) {
-    if (a.M <= CfgTiny::BM) return launch_cfg<CfgTiny>(a, stream);
-    if (a.M <= CfgSmall::BM) return launch_cfg<CfgSmall>(a, stream);
-    return launch_cfg<CfgPrefill>(a, stream);
-}
+hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream) { return launch_form<false>(a, stream); }
+hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream) { return launch_form<true>(a, stream); }
 
-bool gemm_f16_tiles_fit(int64_t M, int64_t N) {
+bool gemm_dec_tiles_fit(int64_t M, int64_t N) {
     const int64_t bm = M <= CfgTiny::BM ? CfgTiny::BM : (M <= CfgSmall::BM ? CfgSmall::BM : CfgPrefill::BM);
     const int64_t bn = M <= CfgSmall::BM ? CfgSmall::BN : CfgPrefill::BN;
     return ((M + bm - 1) / bm) * ((N + bn - 1) / bn) <= (int64_t(1) << 31) - 1;

@@ -299,10 +299,11 @@ hipError_t launch_gemv_multi(const LinearArgs &a, const LayerDesc *layers, int G
                              hipStream_t stream);
 hipError_t launch_gemv_fused_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
                                    hipStream_t stream);
+// the decoded-weight GEMM on the int8 and the fp16 form of the codebook
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
-// whether the f16 GEMM's tile count for (M, N) fits its grid
-bool gemm_f16_tiles_fit(int64_t M, int64_t N);
+// whether its tile count for (M, N) fits the grid
+bool gemm_dec_tiles_fit(int64_t M, int64_t N);
 bool gemm_rq_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_rq(const LinearArgs &a, hipStream_t stream);
 bool skinny_supported(int64_t M, int64_t N, int64_t K);
