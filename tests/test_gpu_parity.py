@@ -268,8 +268,8 @@ def test_mfma_f16_full_size_sampled(w, N, K):
 
 @pytest.mark.parametrize("algo", ["mfma_i8", "mfma_f16"])
 def test_prefill_longest_rows(w, algo):
-    """K = 131072 (512 rotation blocks, 8192 groups per row) through the two exact-bound
-    prefill kernels: random layer bytes in the format's ranges, sampled rows and tokens against
+    """K = 131072 (512 rotation blocks, 8192 groups per row) through the two decoded-weight
+    prefill routes: random layer bytes in the format's ranges, sampled rows and tokens against
     the oracle's product (and, for the int8 route, its int8-codebook reading)."""
     N, K, M = 200, 131072, 300
     a = {"mfma_i8": w.ALGO_MFMA_I8, "mfma_f16": w.ALGO_MFMA_F16}[algo]

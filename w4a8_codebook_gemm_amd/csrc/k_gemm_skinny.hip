@@ -31,7 +31,7 @@
 //    Each wave's next half-block is in flight while it computes one (a ring of two; a third
 //    half-block in flight was 4-11% slower at M = 8 and 32).  At the end the waves' partial
 //    tiles are summed through LDS in wave order (deterministic) and scaled by
-//    2^(ex-8) s_ch s_x.
+//    2^(ex-7) s_ch s_x.
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
 //    Up to 48 tokens the table reads of the next row tile are issued before the current
 //    tile's multiplies and MFMAs (scheduling barriers keep that order).
