@@ -26,7 +26,8 @@ matrices) / measured time per step.  The same line carries:
                 token = one fused multi-layer call per input (248 launches) from one HIP graph,
                 and the same token with one launch per projection (496);
   prefill       M=2048 GEMMs on both MLP shapes: the int8-codebook and fp16-codebook routes
-                (f16 MFMA on decoded weights) and the requantised route (int8 MFMA);
+                (f16 MFMA on decoded weights), the requantised route (int8 MFMA) and the
+                int8-codebook product with the per-group fold (int8 MFMA + vector ALU);
   w8a8          the INT8 ConvRot comparator (same rotation and int8 activations, per-row
                 int8 weights): decode GEMV on both MLP shapes (prepared x_q), a decode step
                 with its prepare launches beside the W4A8 unfused step, and M=2048 GEMMs;
@@ -538,7 +539,8 @@ def prefill(w, torch, S, shapes, M=2048):
     for (n, k) in shapes:
         xq, sx = w.prepare_activation(torch.from_numpy(S.activations(M, k, seed=0)).cuda())
         y = torch.empty((M, n), dtype=torch.float32, device="cuda")
-        for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16"), (w.ALGO_MFMA_RQ, "mfma_rq")):
+        for algo, name in ((w.ALGO_MFMA_I8, "mfma_i8"), (w.ALGO_MFMA_F16, "mfma_f16"), (w.ALGO_MFMA_RQ, "mfma_rq"),
+                           (w.ALGO_MFMA_I8_FOLD, "mfma_i8_fold")):
             g = make_graph(torch, lambda: [w.linear(xq, sx, pl[(n, k)][c], out=y, algo=algo) for c in range(2)])
             t = time_graph(torch, g, 10) / 2
             tops = 2.0 * M * n * k / t / 1e12
@@ -549,7 +551,7 @@ def prefill(w, torch, S, shapes, M=2048):
     # decoded-weight routes on v_mfma_f32_32x32x16_f16 (the int8 route's int8 x int8 products
     # are exact there), the requantised route on v_mfma_i32_32x32x32_i8
     for name, peak, unit, inst in (("mfma_i8", F16_PEAK_TFLOPS, "TOP/s", "f16"), ("mfma_f16", F16_PEAK_TFLOPS, "TFLOP/s", "f16"),
-                                   ("mfma_rq", INT8_PEAK_TOPS, "TOP/s", "i8")):
+                                   ("mfma_rq", INT8_PEAK_TOPS, "TOP/s", "i8"), ("mfma_i8_fold", INT8_PEAK_TOPS, "TOP/s", "i8")):
         mean = float(np.mean([v["tops"] for v in pre.values() if v["algo"] == name]))
         summary[name] = dict(tops=round(mean, 1), mfma=inst, roofline=dict(
             bound="mfma", achieved=round(mean, 1), peak=peak, unit=unit, frac=round(mean / peak, 4)))
@@ -751,7 +753,7 @@ def pmc_pass(w, torch, S, shapes):
     for (n, k), L in ((S.MLP_GATE_UP, blocks[0]["gate"]), (S.MLP_DOWN, blocks[0]["down"])):
         xq, sx = w.prepare_activation(torch.from_numpy(S.activations(2048, k, seed=0)).cuda())
         y = torch.empty((2048, n), dtype=torch.float32, device="cuda")
-        for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ):
+        for algo in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ, w.ALGO_MFMA_I8_FOLD):
             w.linear(xq, sx, L, out=y, algo=algo)
         W8 = w.w8a8_quantize_weight(torch.from_numpy(S.weights(n, k, seed=0)).cuda())
         w.w8a8_linear(xq, sx, W8, out=y, algo=w.ALGO_MFMA_I8)

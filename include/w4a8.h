@@ -92,7 +92,7 @@ typedef enum {
                                  32) */
     W4A8_ALGO_MFMA_SKINNY = 4, /* the same numerics as MFMA_F16 for M <= 64 (batched decode):
                                  16-row weight tiles streamed once, M*K < 2^31 */
-    W4A8_ALGO_MFMA_RQ = 5     /* full-rate int8 MFMA on requantised weights (prefill):
+    W4A8_ALGO_MFMA_RQ = 5,    /* full-rate int8 MFMA on requantised weights (prefill):
                                  q = rint(dec(s_rel) * codebook[idx] / s_cb), s_cb = max|codebook|
                                  / 127, clamped to +-127, one int32 sum per output,
                                  y = ((float)sum * (s_channel * s_cb)) * s_x; K <= 131072.
@@ -100,6 +100,16 @@ typedef enum {
                                  (card A "Why this exists": int8 GEMM + dequantisation step);
                                  like MFMA_I8 an explicit choice whose error is not inside the
                                  4e-3 bound for every input */
+    W4A8_ALGO_MFMA_I8_FOLD = 6 /* the int8-codebook product computed step by step as the int8
+                                 path is described: v_mfma_i32_32x32x16_i8 (K = 16, one group)
+                                 gives the exact int32 partial P = sum x_q * cb_i8[idx] of each
+                                 group, and the vector ALU folds it, acc = fma(dec(s_rel),
+                                 (float)P, acc), group by group; y = acc * s_cb * s_channel *
+                                 s_x.  The same numerics as MFMA_I8 up to the order of the fp32
+                                 additions (identical bits on most outputs, a few ulps apart on
+                                 the rest), at roughly 0.6x its rate: the fold's conversion and
+                                 fma per partial run on the vector ALU.  256 x 192 tiles.  An
+                                 explicit choice */
 } w4a8_algo;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -198,9 +208,9 @@ W4A8_API int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t
 /* As w4a8_linear with an explicit kernel choice (w4a8_algo).  W4A8_ALGO_GEMV returns
  * W4A8_ERR_SHAPE outside its range (M <= 4 and M*K <= 40960), W4A8_ALGO_MFMA_SKINNY outside
  * its range (M <= 64, M*K < 2^31, 40*K < 2^31), W4A8_ALGO_MFMA_RQ for K > 131072 (the
- * int32 sum must stay exact), and the three prefill GEMMs (MFMA_I8, MFMA_F16, MFMA_RQ) for
- * more than 2^31 - 1 workgroup tiles (see the algorithm list for the tile shapes).  An
- * unknown algorithm code returns W4A8_ERR_DTYPE. */
+ * int32 sum must stay exact), and the four prefill GEMMs (MFMA_I8, MFMA_F16, MFMA_RQ,
+ * MFMA_I8_FOLD) for more than 2^31 - 1 workgroup tiles (see the algorithm list for the tile
+ * shapes).  An unknown algorithm code returns W4A8_ERR_DTYPE. */
 W4A8_API int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
                      const int8_t *packed, const uint8_t *s_rel, const float *s_channel,
                      const float *codebook, int64_t N, void *y, int y_dtype, int algo,

@@ -69,6 +69,8 @@ int main(void) {
     EXPECT(lin(FAKE, FAKE, huge, 512, FAKE, FAKE, FAKE, FAKE, huge, FAKE, 0, W4A8_ALGO_MFMA_I8), W4A8_ERR_SHAPE);
     EXPECT(lin(FAKE, FAKE, huge, 512, FAKE, FAKE, FAKE, FAKE, huge, FAKE, 0, W4A8_ALGO_MFMA_F16), W4A8_ERR_SHAPE);
     EXPECT(lin(FAKE, FAKE, huge, 512, FAKE, FAKE, FAKE, FAKE, huge, FAKE, 0, W4A8_ALGO_MFMA_RQ), W4A8_ERR_SHAPE);
+    EXPECT(lin(FAKE, FAKE, huge, 512, FAKE, FAKE, FAKE, FAKE, huge, FAKE, 0, W4A8_ALGO_MFMA_I8_FOLD), W4A8_ERR_SHAPE);
+    EXPECT(lin(FAKE, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 0, 7), W4A8_ERR_DTYPE);
     EXPECT(w4a8_linear(NULL, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, NULL), W4A8_ERR_NULL);
 
     /* prepare, quantize (both forms) */

@@ -90,10 +90,10 @@ def test_linear_validation(L):
         assert lin(L, ptrs={k: MIS}) == 4
     assert lin(L, M=8, K=5120, algo=w.ALGO_GEMV) == 2  # outside the GEMV's range
     assert lin(L, M=65, K=512, algo=w.ALGO_MFMA_SKINNY) == 2  # outside the skinny kernel's
-    assert lin(L, algo=6) == 3
+    assert lin(L, algo=7) == 3
     assert lin(L, M=4, K=131328, algo=w.ALGO_MFMA_RQ) == 2  # the int32 sum would not be exact
     huge = (1 << 31) - 1                                     # 2^31 - 1 tokens and rows: too many tiles
-    for a in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ):
+    for a in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ, w.ALGO_MFMA_I8_FOLD):
         assert lin(L, M=huge, N=huge, algo=a) == 2
     assert L.w4a8_linear(0, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == 1
 

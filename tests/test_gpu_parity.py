@@ -228,21 +228,28 @@ def i8_tight(y, q, xq, sx, rows, toks):
 
 # 256-token x 192-row tiles: ragged in both directions, several tiles each way, K = 256 (one
 # turn of the four-stage ring)
+# the two int8-codebook kernels: the group scale inside the fp16 weight, and the int8 MFMA
+# with the per-group fold on the vector ALU
+I8_ALGOS = {"mfma_i8": 2, "mfma_i8_fold": 6}
+
+
+@pytest.mark.parametrize("algo", list(I8_ALGOS))
 @pytest.mark.parametrize("N,K,M", [(256, 512, 4), (200, 768, 37), (300, 1024, 130), (128, 256, 128),
                                    (385, 1280, 600), (193, 256, 65), (1000, 2048, 513)])
-def test_mfma_i8_parity(w, N, K, M):
-    say(f"mfma_i8 N={N} K={K} M={M}")
-    y, yr, A, (q, xq, sx) = run_linear(w, w.ALGO_MFMA_I8, N, K, M, n_out=2)
+def test_mfma_i8_parity(w, N, K, M, algo):
+    say(f"{algo} N={N} K={K} M={M}")
+    y, yr, A, (q, xq, sx) = run_linear(w, I8_ALGOS[algo], N, K, M, n_out=2)
     assert_gate(y, yr, A)
     i8_tight(y, q, xq, sx, None, None)
 
 
+@pytest.mark.parametrize("algo", list(I8_ALGOS))
 @pytest.mark.parametrize("N,K", [S.MLP_GATE_UP, S.MLP_DOWN])
-def test_mfma_i8_full_size_sampled(w, N, K):
+def test_mfma_i8_full_size_sampled(w, N, K, algo):
     M = 2048
-    say(f"mfma_i8 full N={N} K={K} M={M}")
+    say(f"{algo} full N={N} K={K} M={M}")
     rows, toks = sample(N, 384, N), sample(M, 48, M + 1)
-    y, yr, A, (q, xq, sx) = run_linear(w, w.ALGO_MFMA_I8, N, K, M, rows=rows, toks=toks)
+    y, yr, A, (q, xq, sx) = run_linear(w, I8_ALGOS[algo], N, K, M, rows=rows, toks=toks)
     assert_gate(y, yr, A)
     i8_tight(y, q, xq, sx, rows, toks)
 
@@ -266,13 +273,13 @@ def test_mfma_f16_full_size_sampled(w, N, K):
     assert_gate(y, yr, A)
 
 
-@pytest.mark.parametrize("algo", ["mfma_i8", "mfma_f16"])
+@pytest.mark.parametrize("algo", ["mfma_i8", "mfma_i8_fold", "mfma_f16"])
 def test_prefill_longest_rows(w, algo):
     """K = 131072 (512 rotation blocks, 8192 groups per row) through the two decoded-weight
     prefill routes: random layer bytes in the format's ranges, sampled rows and tokens against
     the oracle's product (and, for the int8 route, its int8-codebook reading)."""
     N, K, M = 200, 131072, 300
-    a = {"mfma_i8": w.ALGO_MFMA_I8, "mfma_f16": w.ALGO_MFMA_F16}[algo]
+    a = {"mfma_i8": w.ALGO_MFMA_I8, "mfma_i8_fold": w.ALGO_MFMA_I8_FOLD, "mfma_f16": w.ALGO_MFMA_F16}[algo]
     say(f"{algo} longest rows N={N} K={K} M={M}")
     g = np.random.default_rng(12)
     packed = g.integers(-128, 128, size=(N, K // 2), dtype=np.int8)
@@ -287,7 +294,7 @@ def test_prefill_longest_rows(w, algo):
     y = y.cpu().numpy().astype(np.float64)[np.ix_(toks, rows)]
     yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb, rows, toks)
     assert_gate(y, yr, A)
-    if algo == "mfma_i8":
+    if algo.startswith("mfma_i8"):
         i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, rows, toks)
 
 
@@ -426,16 +433,16 @@ def test_mfma_skinny_long_rows(w):
     assert_gate(y, yr, A)
 
 
-@pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16", "mfma_skinny"])
+@pytest.mark.parametrize("algo", ["gemv", "mfma_i8", "mfma_f16", "mfma_skinny", "mfma_i8_fold"])
 def test_bf16_output(w, algo):
-    a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3, "mfma_skinny": 4}[algo]
+    a = {"gemv": 1, "mfma_i8": 2, "mfma_f16": 3, "mfma_skinny": 4, "mfma_i8_fold": 6}[algo]
     say(f"bf16 output {algo}")
     y, yr, A, _ = run_linear(w, a, 256, 512, 2, out_dtype=torch.bfloat16, n_out=2)
     assert_gate(y, yr, A, extra=2.0 ** -8 * np.abs(yr))
 
 
-@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (4, 3), (4, 64), (5, 300), (0, 1),
-                                    (0, 8), (0, 300)])
+@pytest.mark.parametrize("algo,M", [(1, 1), (1, 4), (2, 64), (3, 64), (4, 3), (4, 64), (5, 300), (6, 300),
+                                    (0, 1), (0, 8), (0, 300)])
 def test_deterministic_and_auto(w, algo, M):
     say(f"determinism algo={algo} M={M}")
     N, K = 512, 1024
@@ -537,13 +544,14 @@ ALL_FINITE_CODES = [c for c in range(256) if c not in (0x7F, 0xFF)]
 @pytest.mark.parametrize("algo,N,K,M", [("gemv", 300, 1024, 1), ("gemv", 257, 2048, 3),
                                         ("mfma_skinny", 300, 1024, 8), ("mfma_skinny", 1001, 768, 64),
                                         ("mfma_i8", 300, 1024, 300), ("mfma_f16", 300, 1024, 300),
-                                        ("mfma_i8", 200, 768, 8), ("mfma_f16", 200, 768, 8)])
+                                        ("mfma_i8", 200, 768, 8), ("mfma_f16", 200, 768, 8),
+                                        ("mfma_i8_fold", 300, 1024, 300)])
 def test_every_scale_code(w, algo, N, K, M):
     """Random group-scale bytes over every finite E4M3FN code (each appears over a hundred
     times) through each kernel that decodes them with the hardware conversion, against the
     oracle's exact product; the int8 route also against its int8-codebook reading."""
     a = {"gemv": w.ALGO_GEMV, "mfma_skinny": w.ALGO_MFMA_SKINNY, "mfma_i8": w.ALGO_MFMA_I8,
-         "mfma_f16": w.ALGO_MFMA_F16}[algo]
+         "mfma_f16": w.ALGO_MFMA_F16, "mfma_i8_fold": w.ALGO_MFMA_I8_FOLD}[algo]
     say(f"{algo} every scale code N={N} K={K} M={M}")
     packed, s_rel, s_ch, cb = random_layer(N, K, 21 + M, ALL_FINITE_CODES)
     assert len(np.unique(s_rel)) == len(ALL_FINITE_CODES)
@@ -554,7 +562,7 @@ def test_every_scale_code(w, algo, N, K, M):
     y = y.cpu().numpy().astype(np.float64)
     yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb)
     assert_gate(y, yr, A)
-    if algo == "mfma_i8":
+    if algo.startswith("mfma_i8"):
         i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, None, None)
 
 

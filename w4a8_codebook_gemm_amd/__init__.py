@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a8.so")
 
 F32, BF16 = 0, 1
-ALGO_AUTO, ALGO_GEMV, ALGO_MFMA_I8, ALGO_MFMA_F16, ALGO_MFMA_SKINNY, ALGO_MFMA_RQ = 0, 1, 2, 3, 4, 5
+ALGO_AUTO, ALGO_GEMV, ALGO_MFMA_I8, ALGO_MFMA_F16, ALGO_MFMA_SKINNY, ALGO_MFMA_RQ, ALGO_MFMA_I8_FOLD = (
+    0, 1, 2, 3, 4, 5, 6)
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
           5: "ERR_WORKSPACE", 6: "ERR_HIP", 7: "ERR_DEVICE"}
 EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace",
@@ -229,8 +230,9 @@ def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dty
     """y [M, N] = the quantised product of prepared activations with one layer.
 
     algo: ALGO_AUTO (what w4a8_linear picks), ALGO_GEMV, ALGO_MFMA_SKINNY, ALGO_MFMA_F16,
-    ALGO_MFMA_I8 (exact per-16 fold) or ALGO_MFMA_RQ (weights requantised to int8: an
-    approximation of the product, see w4a8.h)."""
+    ALGO_MFMA_I8 (the int8 codebook, group scale folded exactly into the fp16 weight),
+    ALGO_MFMA_I8_FOLD (the same product on int8 MFMA with a per-group fold) or ALGO_MFMA_RQ
+    (weights requantised to int8); the int8 routes approximate the product, see w4a8.h."""
     if x_q.dim() != 2:
         raise ValueError("x_q must be 2-D [M, K]")
     m, k = x_q.shape

@@ -150,7 +150,7 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     if (st != W4A8_OK) return st;
     if (algo == W4A8_ALGO_AUTO) algo = pick(M, N, K);
     if (algo != W4A8_ALGO_GEMV && algo != W4A8_ALGO_MFMA_I8 && algo != W4A8_ALGO_MFMA_F16 &&
-        algo != W4A8_ALGO_MFMA_SKINNY && algo != W4A8_ALGO_MFMA_RQ)
+        algo != W4A8_ALGO_MFMA_SKINNY && algo != W4A8_ALGO_MFMA_RQ && algo != W4A8_ALGO_MFMA_I8_FOLD)
         return W4A8_ERR_DTYPE;
     if (algo == W4A8_ALGO_GEMV && !w4a8::gemv_supported(M, K)) return W4A8_ERR_SHAPE;
     if (algo == W4A8_ALGO_MFMA_SKINNY && !w4a8::skinny_supported(M, N, K)) return W4A8_ERR_SHAPE;
@@ -158,6 +158,8 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     // the decoded-weight GEMMs launch one workgroup per tile (256 x 192, or smaller tiles for
     // few tokens)
     if ((algo == W4A8_ALGO_MFMA_I8 || algo == W4A8_ALGO_MFMA_F16) && !w4a8::gemm_dec_tiles_fit(M, N))
+        return W4A8_ERR_SHAPE;
+    if (algo == W4A8_ALGO_MFMA_I8_FOLD && ((M + 255) / 256) * ((N + 191) / 192) > (int64_t(1) << 31) - 1)
         return W4A8_ERR_SHAPE;
     int num_cu = 0;
     st = current_device(&num_cu);
@@ -171,6 +173,7 @@ int w4a8_linear_algo(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
         case W4A8_ALGO_MFMA_I8: e = w4a8::launch_gemm_i8(a, s); break;
         case W4A8_ALGO_MFMA_SKINNY: e = w4a8::launch_gemm_skinny(a, num_cu, s); break;
         case W4A8_ALGO_MFMA_RQ: e = w4a8::launch_gemm_rq(a, s); break;
+        case W4A8_ALGO_MFMA_I8_FOLD: e = w4a8::launch_gemm_i8_fold(a, s); break;
         default: e = w4a8::launch_gemm_f16(a, s); break;
     }
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;

@@ -302,6 +302,8 @@ hipError_t launch_gemv_fused_multi(const LinearArgs &a, const LayerDesc *layers,
 // the decoded-weight GEMM on the int8 and the fp16 form of the codebook
 hipError_t launch_gemm_i8(const LinearArgs &a, hipStream_t stream);
 hipError_t launch_gemm_f16(const LinearArgs &a, hipStream_t stream);
+// int8 MFMA, exact int32 partial per group of 16, fp32 fold on the vector ALU
+hipError_t launch_gemm_i8_fold(const LinearArgs &a, hipStream_t stream);
 // whether its tile count for (M, N) fits the grid
 bool gemm_dec_tiles_fit(int64_t M, int64_t N);
 bool gemm_rq_supported(int64_t M, int64_t N, int64_t K);
