@@ -35,10 +35,12 @@
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
 //    Up to 48 tokens the table reads of the next row tile are issued before the current
 //    tile's multiplies and MFMAs (scheduling barriers keep that order).
-//  * Start-up: the workgroup's group scales are requested before the first weight loads (a
-//    request behind them waits for them to drain from HBM); they go straight to LDS through
-//    the buffer unit (16 B per lane), so the weight stream carries no 2-byte loads.  The
-//    codebook comes through the scalar cache, outside the in-order vector load counter.
+//  * Start-up: the epilogue's row and token scales, then the workgroup's group scales are
+//    requested before the first weight loads (a request behind them waits for them to drain
+//    from HBM); the group scales go straight to LDS through the buffer unit (16 B per lane),
+//    so the weight stream carries no 2-byte loads.  The codebook comes through the scalar
+//    cache, outside the in-order vector load counter.  The pair table sits in static LDS, so
+//    its address is a constant of every table read.
 #include <type_traits>
 
 #include <atomic>
@@ -90,9 +92,12 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
 template <int NT, int MT16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg) {
     static_assert(WAVES * NT <= kSmemBytes / 1024, "reduction buffer");
-    // pair table (later the wave reduction), then the staged group scales
-    extern __shared__ __align__(16) char smem[];
-    uint8_t *ss = reinterpret_cast<uint8_t *>(smem + kSmemBytes);
+    // pair table (later the wave reduction) in static LDS, whose address folds into every
+    // table read; the staged group scales in the dynamic part
+    __shared__ __align__(16) uint32_t tabs[kSmemBytes / 4];
+    extern __shared__ __align__(16) char dyn[];
+    char *smem = reinterpret_cast<char *>(tabs);
+    uint8_t *ss = reinterpret_cast<uint8_t *>(dyn);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -106,6 +111,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
         (void *)(a.s_rel + r_begin * grpbytes), (short)0, (int)(nrows * grpbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         (void *)a.x_q, (short)0, (int)(M * K), 0x00020000);
+
+    // the epilogue's row and token scales, requested before anything else: thread (i, j) of
+    // the final sums owns row 16 t + i and token 16 u + j (rows past the range, tokens past
+    // M and threads past 256 read zero through the buffer bounds)
+    const int ei = tid & 15, ej = (tid >> 4) & 15;
+    float rsc[NT], sxv[MT16];
+    {
+        const __amdgpu_buffer_rsrc_t rs_c = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.s_ch + r_begin), (short)0, (int)(nrows * 4), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs_sx = __builtin_amdgcn_make_buffer_rsrc((void *)a.s_x, (short)0, (int)(M * 4), 0x00020000);
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            rsc[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_c, (uint32_t)(16 * t + ei) * 4u, 0, 0));
+#pragma unroll
+        for (int u = 0; u < MT16; u++)
+            sxv[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rs_sx, tid < 256 ? (uint32_t)(16 * u + ej) * 4u : kOutside, 0, 0));
+    }
 
     // the codebook (scalar loads), then the group scales of the workgroup's rows (nrows x
     // K/16 contiguous bytes) copied to LDS 1 KiB per wave instruction, all before the first
@@ -275,26 +298,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
     // fastest, so consecutive threads store consecutive y elements.
     float4_t *red = reinterpret_cast<float4_t *>(smem);
     const float scale = ldexpf(1.0f, ex - 7);
-    const int i = tid & 15, j = (tid >> 4) & 15;
-    const int src = 16 * (i >> 2) + j, comp = i & 3;
-    float rsc[NT];
+    const int src = 16 * (ei >> 2) + ej, comp = ei & 3;
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const int64_t r = r_begin + 16 * t + i;
-        rsc[t] = r < r_begin + nrows ? a.s_ch[r] * scale : 0.0f;
-    }
+    for (int t = 0; t < NT; t++) rsc[t] *= scale;
 #pragma unroll
     for (int u = 0; u < MT16; u++) {
         __syncthreads();  // the table, or the previous token tile, is no longer read
 #pragma unroll
         for (int t = 0; t < NT; t++) red[(wave * NT + t) * 64 + lane] = acc[t][u];
         __syncthreads();
-        const int64_t m = 16 * u + j;
+        const int64_t m = 16 * u + ej;
         if (tid < 256 && m < M) {
-            const float sxm = a.s_x[m];
+            const float sxm = sxv[u];
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const int64_t r = r_begin + 16 * t + i;
+                const int64_t r = r_begin + 16 * t + ei;
                 float v = 0.0f;
 #pragma unroll
                 for (int w = 0; w < WAVES; w++) v += red[(w * NT + t) * 64 + src][comp];
@@ -318,12 +336,12 @@ constexpr int waves_for() { return (MT16 == 1 && NT <= 3) ? 16 : (MT16 <= 2 ? 8 
 template <int NT, int MT16>
 hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
-    const int64_t lds = kSmemBytes + skinny_scale_bytes(rows_wg, a.K / kGroup);
+    const int64_t lds = skinny_scale_bytes(rows_wg, a.K / kGroup);
     // set once per kernel instance; concurrent first calls may both set it, which is harmless
     static std::atomic<bool> attr_set{false};
     if (!attr_set.load(std::memory_order_acquire)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_skinny<NT, MT16, W>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsMax);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSkinnyLdsMax - kSmemBytes);
         if (e != hipSuccess) return e;
         attr_set.store(true, std::memory_order_release);
     }
