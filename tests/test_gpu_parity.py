@@ -566,6 +566,32 @@ def test_every_scale_code(w, algo, N, K, M):
         i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, None, None)
 
 
+@pytest.mark.parametrize("algo,M", [("gemv", 1), ("mfma_skinny", 8), ("mfma_skinny", 40), ("mfma_i8", 300),
+                                    ("mfma_f16", 300), ("mfma_i8_fold", 300)])
+def test_every_scale_code_per_row(w, algo, M):
+    """Row r's group scales are all the r-th finite E4M3FN code, so each output row sees one
+    decoded scale alone: a code decoded wrongly (a subnormal flushed to zero, a sign or an
+    exponent off) moves that row's outputs far outside the per-output gate, which a mix of
+    codes within a row could hide behind its larger groups."""
+    a = {"gemv": w.ALGO_GEMV, "mfma_skinny": w.ALGO_MFMA_SKINNY, "mfma_i8": w.ALGO_MFMA_I8,
+         "mfma_f16": w.ALGO_MFMA_F16, "mfma_i8_fold": w.ALGO_MFMA_I8_FOLD}[algo]
+    N, K = 300, 1024
+    say(f"{algo} one scale code per row N={N} K={K} M={M}")
+    packed, s_rel, s_ch, cb = random_layer(N, K, 41 + M, ALL_FINITE_CODES)
+    s_rel[:len(ALL_FINITE_CODES)] = np.asarray(ALL_FINITE_CODES, dtype=np.uint8)[:, None]
+    _, xq, sx = oracle_acts(M, K, 43, 2)
+    L = w.QuantizedLinear(gpu(packed), gpu(s_rel), gpu(s_ch), gpu(cb))
+    y = w.linear(gpu(xq), gpu(sx), L, algo=a)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    yr, A = O.linear_ref(xq, sx, packed, s_rel, s_ch, cb)
+    nonzero = [r for r, c in enumerate(ALL_FINITE_CODES) if c & 0x7F]  # 0x00 and 0x80 decode to zero
+    assert np.all(np.abs(yr[:, nonzero]) > 0)
+    assert_gate(y, yr, A)
+    if algo.startswith("mfma_i8"):
+        i8_tight(y, {"packed": packed, "s_rel": s_rel, "s_ch": s_ch, "cb": cb}, xq, sx, None, None)
+
+
 # ----------------------------------------------------------------------------- benchmarked launches
 
 def test_bench_gate_up_launch_full_size(w):

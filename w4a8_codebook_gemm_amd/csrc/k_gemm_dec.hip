@@ -171,9 +171,9 @@ __global__ __launch_bounds__(C::kThreads) void k_gemm_dec(LinearArgs a, int tile
         if (pdec) {
             const uint32_t sv = st.s >> sshift;
             constexpr float kPre = I8 ? 1.0f : 128.0f;  // exact: a power of two
-            const _Float16 s0 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 0) * kPre);
-            const _Float16 s1 = (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sv, 1) * kPre);
-            const half2_t g0 = {s0, s0}, g1 = {s1, s1};
+            const uint32_t s2 = e4m3x2_to_f16x2(sv, kPre);
+            const half2_t g0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, s2, 0x01000100u));
+            const half2_t g1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, s2, 0x03020302u));
             const uint32_t pw[4] = {st.p.x, st.p.y, st.p.z, st.p.w};
             uint32_t o[16];
 #pragma unroll

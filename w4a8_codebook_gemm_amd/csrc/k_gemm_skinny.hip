@@ -239,10 +239,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
             for (int t = 0; t < NT; t++) {
                 if (t + 1 < NT) reads(t + 1, pr[(t + 1) & 1], srr[(t + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
-                const uint32_t sr = srr[t & 1];
-                const uint32_t s0 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 0) * 128.0f));
-                const uint32_t s1 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 1) * 128.0f));
-                const uint32_t sg[2] = {s0 | (s0 << 16), s1 | (s1 << 16)};
+                const uint32_t s2 = e4m3x2_to_f16x2(srr[t & 1], 128.0f);
+                const uint32_t sg[2] = {__builtin_amdgcn_perm(0u, s2, 0x01000100u), __builtin_amdgcn_perm(0u, s2, 0x03020302u)};
 #pragma unroll
                 for (int st = 0; st < 4; st++) {
                     uint32_t aw[4];
@@ -262,9 +260,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
             // next; a row past N reads stale LDS and feeds no stored output) as fp16 pairs,
             // times 2^7 (exact for every e4m3 value, and at most 448 * 2^7 = 57344)
             const uint32_t sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grpbytes + 8u * (uint32_t)h + 2u * lq);
-            const uint32_t s0 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 0) * 128.0f));
-            const uint32_t s1 = __builtin_bit_cast(uint16_t, (_Float16)(__builtin_amdgcn_cvt_f32_fp8((int)sr, 1) * 128.0f));
-            const uint32_t sg[2] = {s0 | (s0 << 16), s1 | (s1 << 16)};
+            const uint32_t s2 = e4m3x2_to_f16x2(sr, 128.0f);
+            const uint32_t sg[2] = {__builtin_amdgcn_perm(0u, s2, 0x01000100u), __builtin_amdgcn_perm(0u, s2, 0x03020302u)};
             const uint32_t pw[4] = {s.pk[t].x, s.pk[t].y, s.pk[t].z, s.pk[t].w};
 #pragma unroll
             for (int st = 0; st < 4; st++) {
