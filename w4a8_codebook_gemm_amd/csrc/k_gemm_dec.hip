@@ -44,6 +44,7 @@
 // one XCD share weight and activation stages through its L2.
 #include <type_traits>
 
+#include "e4m3_pair.h"
 #include "w4a8_internal.h"
 
 namespace w4a8 {

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 #include <atomic>
+#include "e4m3_pair.h"
 #include "w4a8_internal.h"
 
 namespace w4a8 {

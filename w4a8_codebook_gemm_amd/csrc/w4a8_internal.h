@@ -23,15 +23,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
     return (c & 0x80u) ? -v : v;
 }
 
-// The two E4M3FN codes in bits 0..15 of v (bits 0..7 first), each times a power of two
-// `scale`, as an fp16 pair: one v_cvt_scalef32_pk_f16_fp8 (gfx950's conversions take the OCP
-// format).  Exact for every finite code and scale 1 or 2^7: an e4m3 value has at most 4
-// significant bits and |v| <= 448, so v * 2^7 <= 57344 < 65504 and 2^-9 * 2^0 is an fp16
-// subnormal.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t v, float scale) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, scale, false));
-}
-
 // Round a non-negative finite fp32 to the nearest E4M3FN code, ties to the even code,
 // saturating at 448 (0x7E).  Works on the bit pattern: pick the code exponent, then round
 // the fp32 mantissa to 3 bits (subnormal codes use a fixed 2^-9 quantum).
