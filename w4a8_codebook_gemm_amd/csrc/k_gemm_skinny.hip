@@ -167,8 +167,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
         }
     };
 
+    // every wave's first slot goes out before any wave's second, so that the first
+    // half-blocks of all waves arrive first and the waves start together (a bare barrier
+    // orders the issue only)
     Slot<NT, MT16> R0, R1;
     fetch(h0, R0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     fetch(h0 + S, R1);
 
     // codebook -> fp16 pair table scaled by 2^-ex; wave w writes 16 / WAVES high nibbles
