@@ -147,12 +147,18 @@ int64_t orc_fit_sample(const float *v, int64_t NK, uint64_t seed, float *sample)
  *   repeat: thresholds t_j = (c_j + c_{j+1}) / 2; cell j = { s : t_{j-1} < s <= t_j };
  *           stop if no cell changed since the previous pass; otherwise every non-empty
  *           cell's level becomes its mean (sum from the running prefix sums of the sorted
- *           sample, accumulated left to right, divided by the count); an empty cell keeps
- *           its level;
+ *           sample, divided by the count); an empty cell keeps its level;
  *   at most 100 updates.
+ * The running sums P[i] = s[0] + ... + s[i-1] are fp64 in a blocked order (the cards fix no
+ * order): the sample is cut into blocks of PREFIX_BLOCK values; within a block the sums run
+ * left to right from 0; the block offsets run left to right over the block totals from 0;
+ * P[i + 1] = offset of i's block + block-local sum up to i.  One fp64 add per value more
+ * than a single left-to-right pass, and every block can be summed at the same time.
  * Returns the number of updates; c16 receives the fp64 levels; bounds17 (nullable) the
  * cell boundaries of the last pass (cell j = sorted indices [b_j, b_{j+1})).
  * ------------------------------------------------------------------------------------ */
+#define PREFIX_BLOCK 1024
+
 static int cmp_total(const void *pa, const void *pb) {
     double a = *(const double *)pa, b = *(const double *)pb;
     if (a < b) return -1;
@@ -178,7 +184,18 @@ int orc_lloyd_max16(const float *sample, int64_t S, int max_iters, double *c16,
     for (int64_t i = 0; i < S; i++) s[i] = (double)sample[i];
     qsort(s, (size_t)S, sizeof(double), cmp_total);
     P[0] = 0.0;
-    for (int64_t i = 0; i < S; i++) P[i + 1] = P[i] + s[i];
+    {
+        double off = 0.0;
+        for (int64_t b0 = 0; b0 < S; b0 += PREFIX_BLOCK) {
+            const int64_t b1 = b0 + PREFIX_BLOCK < S ? b0 + PREFIX_BLOCK : S;
+            double run = 0.0;
+            for (int64_t i = b0; i < b1; i++) {
+                run = run + s[i];
+                P[i + 1] = off + run;
+            }
+            off = off + run;
+        }
+    }
 
     double c[LEVELS];
     for (int j = 0; j < LEVELS; j++) c[j] = s[((int64_t)(2 * j + 1) * S) / 32];

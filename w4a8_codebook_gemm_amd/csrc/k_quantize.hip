@@ -18,8 +18,10 @@
 //     arithmetic of step 1, so the normalised values are never stored: the workspace holds
 //     only the sample and its prefix sums, at most 12 MiB whatever N and K.
 //  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans).
-//  4. k_prefix: running fp64 sums of the sorted values, accumulated strictly left to
-//     right by one thread (the order fixes the rounding, which the codebook bits depend on).
+//  4. k_prefix: running fp64 sums of the sorted values in the blocked order (blocks of
+//     kPrefixBlock values summed left to right from 0, the block offsets left to right over
+//     the block totals, then offset + block-local sum; the order fixes the rounding, which
+//     the codebook bits depend on).  One lane per block, so 1024 blocks run at once.
 //  5. k_lloyd: one wave runs Lloyd's iteration in fp64 from the mid-quantile start:
 //     thresholds (c_j + c_{j+1}) / 2, cell bounds by binary search over the sorted values,
 //     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
@@ -248,24 +250,68 @@ __global__ __launch_bounds__(kSortTile / 2) void k_bitonic_tile(uint32_t *keys, 
 }
 
 // Running fp64 sums P[0] = 0, P[i+1] = P[i] + value(i), strictly in index order.
-__global__ __launch_bounds__(256) void k_prefix(const uint32_t *__restrict__ keys, int64_t S,
-                                                double *__restrict__ P) {
-    constexpr int kChunk = 4096;
-    __shared__ double buf[kChunk];
+constexpr int kPrefixBlock = 1024;
+constexpr int kPrefixThreads = (int)(kSampleMax / kPrefixBlock);  // one lane per block
+
+// One lane's pass over its block [b0, b1): the left-to-right fp64 chain from 0; with
+// WRITE, P[i + 1] = off + (chain up to i).  The keys come 16 bytes per load, the next 32
+// values requested while the current 32 are summed (the prefetch address is clamped to the
+// block, so every load is issued on every path).
+template <bool WRITE>
+__device__ __forceinline__ double prefix_pass(const uint32_t *__restrict__ keys, int64_t b0, int64_t b1,
+                                              double off, double *__restrict__ P) {
+    constexpr int kG = 32;
     double run = 0.0;
-    if (threadIdx.x == 0) P[0] = 0.0;
-    for (int64_t c0 = 0; c0 < S; c0 += kChunk) {
-        const int n = (int)((S - c0) < kChunk ? (S - c0) : kChunk);
-        for (int i = threadIdx.x; i < n; i += blockDim.x) buf[i] = (double)key_to_f32(keys[c0 + i]);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int i = 0; i < n; i++) {
-                run = run + buf[i];
-                P[c0 + i + 1] = run;
-            }
+    const int64_t nfull = b0 + ((b1 - b0) / kG) * kG;
+    const uint4 *k4 = reinterpret_cast<const uint4 *>(keys);  // b0 is a multiple of 1024
+    uint4 cur[kG / 4], nxt[kG / 4];
+    const int64_t first = b0 < nfull ? b0 : 0;
+#pragma unroll
+    for (int q = 0; q < kG / 4; q++) cur[q] = k4[first / 4 + q];
+    for (int64_t i = b0; i < nfull; i += kG) {
+        const int64_t j = i + kG < nfull ? i + kG : i;
+#pragma unroll
+        for (int q = 0; q < kG / 4; q++) nxt[q] = k4[j / 4 + q];
+#pragma unroll
+        for (int k = 0; k < kG; k++) {
+            const uint4 w = cur[k >> 2];
+            const uint32_t key = (k & 3) == 0 ? w.x : (k & 3) == 1 ? w.y : (k & 3) == 2 ? w.z : w.w;
+            run = run + (double)key_to_f32(key);
+            if (WRITE) P[i + k + 1] = off + run;
         }
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kG / 4; q++) cur[q] = nxt[q];
     }
+    for (int64_t i = nfull; i < b1; i++) {
+        run = run + (double)key_to_f32(keys[i]);
+        if (WRITE) P[i + 1] = off + run;
+    }
+    return run;
+}
+
+// P[0] = 0; P[i + 1] = off[b] + (s[b0] + ... + s[i]) for i in block b = [b0, b0 + 1024),
+// the block-local sum running left to right from 0 and off[b] = tot[0] + ... + tot[b - 1]
+// running left to right from 0 over the block totals.  Each lane runs its block's chain
+// twice (once for the total, once for the outputs) rather than storing and re-reading it.
+__global__ __launch_bounds__(kPrefixThreads) void k_prefix(const uint32_t *__restrict__ keys, int64_t S,
+                                                           double *__restrict__ P) {
+    __shared__ double tot[kPrefixThreads], offs[kPrefixThreads];
+    const int t = threadIdx.x;
+    const int nb = (int)((S + kPrefixBlock - 1) / kPrefixBlock);
+    const int64_t b0 = (int64_t)t * kPrefixBlock;
+    const int64_t b1 = b0 + kPrefixBlock < S ? b0 + kPrefixBlock : S;
+    if (t < nb) tot[t] = prefix_pass<false>(keys, b0, b1, 0.0, P);
+    __syncthreads();
+    if (t == 0) {
+        double off = 0.0;
+        for (int b = 0; b < nb; b++) {
+            offs[b] = off;
+            off = off + tot[b];
+        }
+        P[0] = 0.0;
+    }
+    __syncthreads();
+    if (t < nb) prefix_pass<true>(keys, b0, b1, offs[t], P);
 }
 
 __device__ __forceinline__ int64_t count_le(const uint32_t *keys, int64_t S, double t) {
@@ -408,7 +454,7 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    hipLaunchKernelGGL(k_prefix, dim3(1), dim3(256), 0, stream, keys, L.S, P);
+    hipLaunchKernelGGL(k_prefix, dim3(1), dim3(kPrefixThreads), 0, stream, keys, L.S, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_lloyd, dim3(1), dim3(64), 0, stream, keys, P, L.S, cb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
