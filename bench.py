@@ -430,7 +430,8 @@ def decode(w, torch, S, args, shapes):
 
 
 def sweep(w, torch, S):
-    """Batched decode: every kernel that supports (M, shape), and the automatic choice."""
+    """Batched decode: every kernel that supports (M, shape), the K-split skinny kernel of
+    w4a8_linear_ws where it applies, and the automatic choice of w4a8_forward."""
     shapes = [S.MLP_GATE_UP, S.MLP_DOWN, S.ATTN_SQUARE, S.ATTN_WIDE]
     layers = build_layers(w, torch, shapes, COPIES)
     algos = (("gemv", w.ALGO_GEMV), ("mfma_skinny", w.ALGO_MFMA_SKINNY), ("mfma_i8", w.ALGO_MFMA_I8),
@@ -451,6 +452,11 @@ def sweep(w, torch, S):
                         raise
                     continue
                 point[name] = round(time_kernel_graph(torch, g) / COPIES * 1e6, 2)
+            ws = w.linear_workspace(m, n, k)  # the K-split batched decode (one workspace: calls run in order)
+            if ws is not None:
+                g = make_graph(torch, lambda: [w.linear_ws(xq, sx, layers[(n, k)][c], ws, out=y)
+                                               for c in range(COPIES)])
+                point["mfma_skinny_split"] = round(time_kernel_graph(torch, g) / COPIES * 1e6, 2)
             g = make_graph(torch, lambda: [w.forward(x, layers[(n, k)][c], out=y, x_q=xq, s_x=sx)
                                            for c in range(COPIES)])
             t_auto = time_kernel_graph(torch, g) / COPIES

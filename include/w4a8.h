@@ -231,6 +231,40 @@ W4A8_API int w4a8_forward(const void *x, int x_dtype, int64_t M, int64_t K, cons
                           const uint8_t *s_rel, const float *s_channel, const float *codebook,
                           int64_t N, void *y, int y_dtype, int8_t *x_q, float *s_x, void *stream);
 
+/*
+ * Workspace bytes w4a8_linear_ws can use for (M, N, K) on the current device, or 0 when the
+ * algorithm w4a8_linear picks needs none (a negative status for an invalid shape).  Only
+ * the batched-decode kernel uses one, from 17 to 64 tokens: where a workgroup would own few
+ * rows (under 80 per compute unit, as for the MLP down projection) and K is long (a multiple
+ * of 1024, at least 8192), it splits K into 4 parts, each workgroup taking full row tiles
+ * over one part, so that every compute unit reads a quarter of the activations.  Launches
+ * nothing.
+ */
+W4A8_API int64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w4a8_linear with a workspace [the same product and card sections as w4a8_linear].
+ *
+ *  workspace        device memory, 16-byte aligned, of workspace_bytes bytes: 4 KiB of
+ *                   arrival counters, then the parts' sums.  It must be zero-filled before
+ *                   its first use; every call that completes leaves the counters at zero, so
+ *                   one workspace serves any later shape it is large enough for.  Calls that
+ *                   overlap in time (other streams, other threads) need workspaces of their
+ *                   own.
+ *  workspace_bytes  at least w4a8_linear_workspace_bytes(M, N, K) to split K; with less (or
+ *                   a NULL workspace) the call runs exactly as w4a8_linear.
+ *
+ * With the split, each part's workgroup stores its partial sums (fp32, before the row and
+ * token scales) in the workspace and counts its arrival on an atomic counter of its row
+ * block; the last part to arrive adds the parts' sums in part order, scales them and
+ * writes y.  The result depends on the part order only, not on the order of arrival, so it
+ * is deterministic; it differs from w4a8_linear's only by the order of fp32 additions and
+ * meets the same bound.
+ */
+W4A8_API int w4a8_linear_ws(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
+                            const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                            void *y, int y_dtype, void *workspace, int64_t workspace_bytes, void *stream);
+
 /* The algorithm w4a8_linear picks for (M, N, K) on the current device, or a negative
  * status if the shape is invalid.  Launches nothing. */
 W4A8_API int w4a8_linear_pick(int64_t M, int64_t N, int64_t K);

@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 14 and set(names) == set(w.EXPORTS)
+    assert len(names) == 16 and set(names) == set(w.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
 
@@ -96,6 +96,23 @@ def test_linear_validation(L):
     for a in (w.ALGO_MFMA_I8, w.ALGO_MFMA_F16, w.ALGO_MFMA_RQ, w.ALGO_MFMA_I8_FOLD):
         assert lin(L, M=huge, N=huge, algo=a) == 2
     assert L.w4a8_linear(0, FAKE, 4, 512, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == 1
+
+
+def test_linear_ws_validation(L):
+    """The workspace entry points validate like w4a8_linear, plus the workspace's alignment,
+    before any HIP call; a shape the batched-decode kernel does not take needs no workspace."""
+    ws = lambda wsp=FAKE, nb=1 << 20, **kw: L.w4a8_linear_ws(
+        FAKE if "xq" not in kw else kw["xq"], FAKE, kw.get("M", 4), kw.get("K", 512), FAKE, FAKE, FAKE, FAKE,
+        kw.get("N", 4), FAKE, kw.get("ydt", 0), wsp, nb, None)
+    assert ws(xq=0) == 1
+    for M, K, N in [(0, 512, 4), (4, 4304, 4), (4, 128, 4), (4, 512, 0)]:
+        assert ws(M=M, K=K, N=N) == 2
+    assert ws(ydt=7) == 3
+    assert ws(wsp=MIS) == 4
+    for M, K, N in [(0, 512, 4), (4, 100, 4), (4, 512, 0)]:
+        assert L.w4a8_linear_workspace_bytes(M, N, K) == -2
+    assert L.w4a8_linear_workspace_bytes(1, 5120, 5120) == 0     # the GEMV
+    assert L.w4a8_linear_workspace_bytes(2048, 5120, 5120) == 0  # a prefill GEMM
 
 
 def test_prepare_and_quantize_validation(L):

@@ -411,6 +411,74 @@ def test_mfma_skinny_full_size_sampled(w, N, K, M):
     assert_gate(y, yr, A)
 
 
+# shapes whose batched decode splits K in 4 on a 256-CU device (more than 16 tokens, K a
+# multiple of 1024 of at least 8192, few rows per CU), ragged row blocks and token tiles
+# included
+SPLIT_CASES = [(1000, 8192, 24, 4), (300, 8192, 40, 4), (5120, 8192, 17, 4), (77, 8192, 64, 4)]
+
+
+def run_linear_ws(w, N, K, M, rows=None, out_dtype=torch.float32, seed=0, n_out=None, ws=None):
+    _, q = oracle_layer(N, K, seed)
+    _, xq, sx = oracle_acts(M, K, seed, n_out)
+    L = gpu_layer(w, q)
+    if ws is None:
+        ws = w.linear_workspace(M, N, K)
+    y = w.linear_ws(gpu(xq), gpu(sx), L, ws, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        y = y[:, rows]
+    yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows)
+    return y, yr, A, ws
+
+
+def counters_clear(ws, M, N, parts):
+    """The arrival counters (the workspace's first 4 KiB, before the parts' sums) are all back
+    to zero."""
+    assert ws.numel() == 4096 + parts * M * N * 4
+    return int(ws[:4096].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("N,K,M,parts", SPLIT_CASES)
+def test_mfma_skinny_split_parity(w, N, K, M, parts):
+    """The batched decode with K split across workgroups (w4a8_linear_ws): within the gate,
+    the workspace's counters back at zero, two calls in a row (the second on a smaller
+    input sharing the workspace) and a repeat bit-identical."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    if ncu != 256:
+        pytest.skip(f"split shapes chosen for 256 compute units, this device has {ncu}")
+    say(f"mfma_skinny split N={N} K={K} M={M} parts={parts}")
+    nb = w.linear_workspace_bytes(M, N, K)
+    assert nb == 4096 + parts * M * N * 4
+    y, yr, A, ws = run_linear_ws(w, N, K, M, n_out=2)
+    assert_gate(y, yr, A)
+    assert counters_clear(ws, M, N, parts)
+    y2, yr2, A2, _ = run_linear_ws(w, N, K, max(4, M // 2), seed=1, ws=ws)
+    assert_gate(y2, yr2, A2)
+    y3, _, _, _ = run_linear_ws(w, N, K, M, n_out=2, ws=ws)
+    assert np.array_equal(y, y3)
+    assert counters_clear(ws, M, N, parts)
+
+
+def test_mfma_skinny_split_full_size_and_fallback(w):
+    """The MLP down projection at 64 tokens splits K in 4; bf16 output; with no workspace (or
+    one too small) linear_ws runs as linear does, bit for bit."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    if ncu != 256:
+        pytest.skip(f"split shapes chosen for 256 compute units, this device has {ncu}")
+    N, K, M = 5120, 17408, 64
+    say(f"mfma_skinny split full N={N} K={K} M={M}")
+    rows = sample(N, 512, N + M)
+    y, yr, A, ws = run_linear_ws(w, N, K, M, rows=rows)
+    assert_gate(y, yr, A)
+    yb, yrb, Ab, _ = run_linear_ws(w, N, K, M, rows=rows, out_dtype=torch.bfloat16, ws=ws)
+    assert_gate(yb, yrb, Ab, extra=2.0 ** -8 * np.abs(yrb))
+    assert counters_clear(ws, M, N, 4)
+    y0, _, _, _ = run_linear_ws(w, N, K, M, rows=rows, ws=torch.zeros(0, dtype=torch.uint8, device="cuda"))
+    y1, _, _, _ = run_linear(w, w.ALGO_AUTO, N, K, M, rows=rows)
+    assert np.array_equal(y0, y1)
+
+
 def test_mfma_skinny_long_rows(w):
     """Rows so long that a workgroup's staged group scales leave room for fewer row tiles
     (12304 x 32768 wants four 16-row tiles per workgroup; three fit beside the table).  The

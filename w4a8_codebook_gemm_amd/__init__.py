@@ -31,7 +31,7 @@ EXPORTS = ("w4a8_version", "w4a8_status_string", "w4a8_quantize_weight_workspace
            "w4a8_quantize_weight", "w4a8_prepare_activation", "w4a8_linear",
            "w4a8_linear_algo", "w4a8_linear_pick", "w4a8_forward", "w4a8_linear_multi",
            "w4a8_forward_multi", "w4a8_w8a8_quantize_weight", "w4a8_w8a8_linear",
-           "w4a8_quantize_weight_noalloc")
+           "w4a8_quantize_weight_noalloc", "w4a8_linear_workspace_bytes", "w4a8_linear_ws")
 MAX_GROUP = 8
 
 
@@ -76,6 +76,10 @@ def lib():
         L.w4a8_linear_algo.restype = i32
         L.w4a8_linear_pick.argtypes = [i64, i64, i64]
         L.w4a8_linear_pick.restype = i32
+        L.w4a8_linear_workspace_bytes.argtypes = [i64, i64, i64]
+        L.w4a8_linear_workspace_bytes.restype = i64
+        L.w4a8_linear_ws.argtypes = [P, P, i64, i64, P, P, P, P, i64, P, i32, P, i64, P]
+        L.w4a8_linear_ws.restype = i32
         L.w4a8_forward.argtypes = [P, i32, i64, i64, P, P, P, P, i64, P, i32, P, P, P]
         L.w4a8_forward.restype = i32
         L.w4a8_linear_multi.argtypes = [P, P, i64, i64, i32, P, i32, P]
@@ -246,6 +250,45 @@ def linear(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, out_dty
     with torch.cuda.device(dev):
         _check(lib().w4a8_linear_algo(xqp, sxp, m, k, pp, sp, cp, bp, n, yp, _fdtype(out), algo, _stream()),
                "w4a8_linear")
+    return out
+
+
+def linear_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Workspace bytes linear_ws can use for (M, N, K) on the current device (0: none)."""
+    v = lib().w4a8_linear_workspace_bytes(m, n, k)
+    if v < 0:
+        _check(-v, "w4a8_linear_workspace_bytes")
+    return v
+
+
+def linear_workspace(m: int, n: int, k: int, device=None) -> torch.Tensor | None:
+    """A zero-filled workspace for linear_ws (None when the shape needs none)."""
+    nb = linear_workspace_bytes(m, n, k)
+    return torch.zeros(nb, dtype=torch.uint8, device=device or "cuda") if nb else None
+
+
+def linear_ws(x_q: torch.Tensor, s_x: torch.Tensor, layer: QuantizedLinear, workspace: torch.Tensor | None,
+              out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """linear with a workspace (from linear_workspace; one per concurrent call): the batched
+    decode of layers with few rows per compute unit then splits K (see w4a8_linear_ws)."""
+    if x_q.dim() != 2:
+        raise ValueError("x_q must be 2-D [M, K]")
+    m, k = x_q.shape
+    dev = x_q.device
+    xqp = _dev(x_q, "x_q", (torch.int8,))
+    sxp = _dev(s_x, "s_x", (torch.float32,), (m,), dev)
+    n, pp, sp, cp, bp = _layer_ptrs(layer, k, dev)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    yp = _dev(out, "y", (torch.float32, torch.bfloat16), (m, n), dev)
+    wsp, wsn = 0, 0
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the device of x_q")
+        wsp, wsn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        _check(lib().w4a8_linear_ws(xqp, sxp, m, k, pp, sp, cp, bp, n, yp, _fdtype(out), wsp, wsn, _stream()),
+               "w4a8_linear_ws")
     return out
 
 

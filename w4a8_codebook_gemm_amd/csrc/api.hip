@@ -298,6 +298,38 @@ int w4a8_w8a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, 
     return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
 }
 
+int64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || !valid_k(K)) return -W4A8_ERR_SHAPE;
+    if (pick(M, N, K) != W4A8_ALGO_MFMA_SKINNY) return 0;
+    int num_cu = 0;
+    int st = current_device(&num_cu);
+    if (st != W4A8_OK) return -st;
+    return w4a8::skinny_workspace_bytes(M, N, K, num_cu);
+}
+
+int w4a8_linear_ws(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
+                   const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
+                   void *y, int y_dtype, void *workspace, int64_t workspace_bytes, void *stream) {
+    int st = check_linear(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype);
+    if (st != W4A8_OK) return st;
+    if (workspace && !aligned16(workspace)) return W4A8_ERR_ALIGN;
+    int num_cu = 0;
+    st = current_device(&num_cu);
+    if (st != W4A8_OK) return st;
+    const int64_t need = pick(M, N, K) == W4A8_ALGO_MFMA_SKINNY ? w4a8::skinny_workspace_bytes(M, N, K, num_cu) : 0;
+    if (need == 0 || !workspace || workspace_bytes < need)
+        return w4a8_linear_algo(x_q, s_x, M, K, packed, s_rel, s_channel, codebook, N, y, y_dtype,
+                                W4A8_ALGO_AUTO, stream);
+    const int q = w4a8::skinny_split(M, N, K, num_cu);
+    w4a8::LinearArgs a{x_q, s_x, M, K, N, packed, s_rel, s_channel, codebook, y, y_dtype == W4A8_BF16,
+                       nullptr, 0, nullptr, nullptr};
+    a.ksplit = q;
+    a.ws_cnt = static_cast<uint32_t *>(workspace);
+    a.ws_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + w4a8::kSkinnyCounterBytes);
+    hipError_t e = w4a8::launch_gemm_skinny(a, num_cu, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
 int w4a8_linear(const int8_t *x_q, const float *s_x, int64_t M, int64_t K, const int8_t *packed,
                 const uint8_t *s_rel, const float *s_channel, const float *codebook, int64_t N,
                 void *y, int y_dtype, void *stream) {

@@ -102,9 +102,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lq = lane >> 4;
     const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t r_begin = (int64_t)blockIdx.x * rows_wg;
+    // with a split of K, workgroup b takes part ks = b % ksplit of K for row block b / ksplit
+    const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
+    const int ks = (int)(blockIdx.x % (unsigned)ksplit), rb = (int)(blockIdx.x / (unsigned)ksplit);
+    const int64_t r_begin = (int64_t)rb * rows_wg;
     const int nrows = (int)min((int64_t)rows_wg, N - r_begin);
     const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
+    const uint32_t grs = grpbytes / (uint32_t)ksplit;  // group-scale bytes of a row in this part
 
     const __amdgpu_buffer_rsrc_t rs_p = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.packed + r_begin * rowbytes), (short)0, (int)(nrows * rowbytes), 0x00020000);
@@ -138,22 +142,25 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
     float cbv[kLevels];
 #pragma unroll
     for (int q = 0; q < kLevels; q++) cbv[q] = cbk[q];
-    const int nsc = (int)(nrows * grpbytes / 16);
-    for (int blk = 64 * wave; blk < nsc; blk += 64 * WAVES)
+    const int nsc = (int)(nrows * grs / 16);
+    const uint32_t cpr = grs / 16;  // 16-byte chunks per row of this part
+    for (int blk = 64 * wave; blk < nsc; blk += 64 * WAVES) {
+        const uint32_t c = (uint32_t)(blk + lane), row = c / cpr;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (__attribute__((address_space(3))) void *)(ss + 16 * blk), 16,
-                                                 16u * (uint32_t)(blk + lane), 0, 0, kNT);
+                                                 row * grpbytes + (uint32_t)ks * grs + 16u * (c - row * cpr), 0, 0, kNT);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // this wave's share of the 128-k half-blocks: every WAVES-th one, so that at any time
     // the workgroup's waves read adjacent 64-B pieces of the same rows (long DRAM runs, and
     // both halves of each 128-B line close together)
-    const int nhalf = (int)(K / 128);
+    const int nhalf = (int)(K / 128) / ksplit, hb = ks * nhalf;  // this part's half-blocks
     const int h0 = wave, h1 = nhalf;
     constexpr int S = WAVES;
 
     auto fetch = [&](int h, Slot<NT, MT16> &s) {
         const bool valid = h < h1;
-        const uint32_t kb = (uint32_t)h * 64u + 16u * lq;  // packed byte within the row
+        const uint32_t kb = (uint32_t)(hb + h) * 64u + 16u * lq;  // packed byte within the row
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const uint32_t row = (uint32_t)(16 * t + li);
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
         }
 #pragma unroll
         for (int u = 0; u < MT16; u++) {
-            const uint32_t off = (uint32_t)(16 * u + li) * (uint32_t)K + (uint32_t)h * 128u + 32u * lq;
+            const uint32_t off = (uint32_t)(16 * u + li) * (uint32_t)K + (uint32_t)(hb + h) * 128u + 32u * lq;
             s.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, valid ? off : kOutside, 0, 0);
             s.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(rs_x, valid ? off + 16u : kOutside, 0, 0);
         }
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
             // off at four token tiles, where the extra registers cost more than it saves)
             uint32_t pr[2][16], srr[2];
             auto reads = [&](int t, uint32_t (&p)[16], uint32_t &sr) {
-                sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grpbytes + 8u * (uint32_t)h + 2u * lq);
+                sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grs + 8u * (uint32_t)h + 2u * lq);
                 const uint32_t pw[4] = {s.pk[t].x, s.pk[t].y, s.pk[t].z, s.pk[t].w};
 #pragma unroll
                 for (int st = 0; st < 4; st++)
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
             // group scales of this lane's 32 values (row 16 t + li, groups 8 h + 2 lq and the
             // next; a row past N reads stale LDS and feeds no stored output) as fp16 pairs,
             // times 2^7 (exact for every e4m3 value, and at most 448 * 2^7 = 57344)
-            const uint32_t sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grpbytes + 8u * (uint32_t)h + 2u * lq);
+            const uint32_t sr = *reinterpret_cast<const uint16_t *>(ss + (16 * t + li) * grs + 8u * (uint32_t)h + 2u * lq);
             const uint32_t s2 = e4m3x2_to_f16x2(sr, 128.0f);
             const uint32_t sg[2] = {__builtin_amdgcn_perm(0u, s2, 0x01000100u), __builtin_amdgcn_perm(0u, s2, 0x03020302u)};
             const uint32_t pw[4] = {s.pk[t].x, s.pk[t].y, s.pk[t].z, s.pk[t].w};
@@ -321,13 +328,72 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
 #pragma unroll
                 for (int w = 0; w < WAVES; w++) v += red[(w * NT + t) * 64 + src][comp];
                 if (r < r_begin + nrows) {
-                    const float val = (v * rsc[t]) * sxm;
-                    if (a.y_bf16)
-                        static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(val);
-                    else
-                        static_cast<float *>(a.y)[m * N + r] = val;
+                    if (ksplit > 1) {
+                        // this part's sum, stored coherently across XCDs (device-scope atomic
+                        // store: written through the XCD's L2, no cache-wide flush)
+                        __hip_atomic_store(a.ws_part + ((int64_t)ks * M + m) * N + r, v, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        const float val = (v * rsc[t]) * sxm;
+                        if (a.y_bf16)
+                            static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(val);
+                        else
+                            static_cast<float *>(a.y)[m * N + r] = val;
+                    }
                 }
             }
+        }
+    }
+    if (ksplit > 1) {
+        // The last part of the row block to arrive adds the parts' sums in part order (so
+        // the result does not depend on the order of arrival) and writes y.  The counter
+        // wraps to 0 on the last arrival, leaving the workspace as it was found.
+        // the flag lives in the staged-scale area (no longer read): a static LDS variable
+        // would push static + dynamic LDS past the 160 KiB the launch asks for
+        int *last = reinterpret_cast<int *>(dyn);
+        // every store of this part has completed (reached the device's coherence point)
+        // before its arrival counts; the loads of the last part are issued after the count
+        // that makes it last, so they see every part.  Device-scope fences would instead
+        // write back and invalidate the whole L2 of every XCD.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) *last = atomicInc(a.ws_cnt + rb, (unsigned)(ksplit - 1)) == (unsigned)(ksplit - 1);
+        __syncthreads();
+        if (*last) {
+            // every part's sums of all this thread's outputs are requested at once (one
+            // memory round trip), then added in part order
+            constexpr int kMaxParts = 4;
+            float pv[MT16][NT][kMaxParts];
+#pragma unroll
+            for (int u = 0; u < MT16; u++)
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const int64_t m = 16 * u + ej, r = r_begin + 16 * t + ei;
+                    const bool ok = tid < 256 && m < M && r < r_begin + nrows;
+#pragma unroll
+                    for (int q = 0; q < kMaxParts; q++)
+                        pv[u][t][q] = ok && q < ksplit ? __hip_atomic_load(a.ws_part + ((int64_t)q * M + m) * N + r,
+                                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                       : 0.0f;
+                }
+#pragma unroll
+            for (int u = 0; u < MT16; u++)
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const int64_t m = 16 * u + ej, r = r_begin + 16 * t + ei;
+                    if (tid < 256 && m < M && r < r_begin + nrows) {
+                        float v = pv[u][t][0];
+#pragma unroll
+                        for (int q = 1; q < kMaxParts; q++)
+                            if (q < ksplit) v += pv[u][t][q];
+                        const float val = (v * rsc[t]) * sxv[u];
+                        if (a.y_bf16)
+                            static_cast<uint16_t *>(a.y)[m * N + r] = f32_to_bf16_rne(val);
+                        else
+                            static_cast<float *>(a.y)[m * N + r] = val;
+                    }
+                }
         }
     }
 }
@@ -340,7 +406,7 @@ constexpr int waves_for() { return (MT16 == 1 && NT <= 3) ? 16 : (MT16 <= 2 ? 8 
 template <int NT, int MT16>
 hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
-    const int64_t lds = skinny_scale_bytes(rows_wg, a.K / kGroup);
+    const int64_t lds = skinny_scale_bytes(rows_wg, a.K / kGroup / (a.ksplit > 1 ? a.ksplit : 1));
     // set once per kernel instance; concurrent first calls may both set it, which is harmless
     static std::atomic<bool> attr_set{false};
     if (!attr_set.load(std::memory_order_acquire)) {
@@ -374,16 +440,43 @@ bool skinny_supported(int64_t M, int64_t N, int64_t K) {
            kSmemBytes + skinny_scale_bytes(16, K / kGroup) <= kSkinnyLdsMax;
 }
 
+int skinny_split(int64_t M, int64_t N, int64_t K, int num_cu) {
+    // K split into 4 parts when a workgroup would otherwise own few rows and K is long: each
+    // part then takes up to kMaxTiles full tiles over a quarter of K, so every CU reads a
+    // quarter of the activations and no tile is mostly padding; each wave keeps at least two
+    // half-blocks of its part.  Measured on the sweep shapes, the split pays from 17 tokens
+    // on (5120 x 17408); with two parts, or fewer tokens, the parts' final sums cost more
+    // than it saves.
+    constexpr int q = 4;
+    if (!skinny_supported(M, N, K) || M <= 16) return 1;
+    const int64_t rows1 = (N + num_cu - 1) / num_cu, rows = (N * q + num_cu - 1) / num_cu;
+    if (rows <= 16 * kMaxTiles && rows > rows1 && K % (256 * q) == 0 && K / 128 / q >= 16 &&
+        kSmemBytes + skinny_scale_bytes(rows, K / kGroup / q) <= kSkinnyLdsMax &&
+        (N + rows - 1) / rows <= kSkinnyCounterBytes / 4)
+        return q;
+    return 1;
+}
+
+int64_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int num_cu) {
+    // the arrival counters first, at a fixed place and size whatever the shape (so that a
+    // workspace can serve shapes of different sizes: no part's sums ever land on a counter),
+    // then the parts' sums
+    const int q = skinny_split(M, N, K, num_cu);
+    return q == 1 ? 0 : kSkinnyCounterBytes + (int64_t)q * M * N * 4;
+}
+
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
     if (!skinny_supported(a.M, a.N, a.K)) return hipErrorInvalidValue;
-    // rows per workgroup: an equal share for every CU, at most kMaxTiles tiles (and fewer
-    // for long rows: the staged scales of a workgroup's rows must fit in LDS)
-    int64_t rows = (a.N + num_cu - 1) / num_cu;
+    const int q = a.ksplit > 1 ? a.ksplit : 1;
+    if (q > 1 && (a.K % (256 * q) != 0 || !a.ws_part || !a.ws_cnt)) return hipErrorInvalidValue;
+    // rows per workgroup: an equal share for every CU (per part of K), at most kMaxTiles
+    // tiles
+    int64_t rows = (a.N * q + num_cu - 1) / num_cu;
     if (rows > 16 * kMaxTiles) rows = 16 * kMaxTiles;
-    while (rows > 16 && kSmemBytes + skinny_scale_bytes(rows, a.K / kGroup) > kSkinnyLdsMax) rows -= 16;
+    while (rows > 16 && kSmemBytes + skinny_scale_bytes(rows, a.K / kGroup / q) > kSkinnyLdsMax) rows -= 16;
     if (rows < 1) rows = 1;
     const int64_t nt = (rows + 15) / 16;
-    const unsigned grid = (unsigned)((a.N + rows - 1) / rows);
+    const unsigned grid = (unsigned)(((a.N + rows - 1) / rows) * q);
     switch (nt) {
         case 1: return launch_nt<1>(a, grid, (int)rows, stream);
         case 2: return launch_nt<2>(a, grid, (int)rows, stream);

@@ -276,6 +276,11 @@ struct LinearArgs {
     int x_bf16;
     int8_t *x_q_out;
     float *s_x_out;
+    // batched decode with K split into ksplit parts: the parts' sums [ksplit][M][N] and one
+    // arrival counter per row block (zero between calls)
+    float *ws_part = nullptr;
+    uint32_t *ws_cnt = nullptr;
+    int ksplit = 1;
 };
 
 bool gemv_supported(int64_t M, int64_t K);
@@ -309,6 +314,9 @@ bool gemm_dec_tiles_fit(int64_t M, int64_t N);
 bool gemm_rq_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_rq(const LinearArgs &a, hipStream_t stream);
 bool skinny_supported(int64_t M, int64_t N, int64_t K);
+constexpr int64_t kSkinnyCounterBytes = 4096;  // the split's arrival counters: 1024 row blocks
+int skinny_split(int64_t M, int64_t N, int64_t K, int num_cu);
+int64_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int num_cu);
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream);
 
 // W8A8 comparator (per-row int8 weights of the rotated rows, no codebook)
