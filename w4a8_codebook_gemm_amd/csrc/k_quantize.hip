@@ -18,11 +18,11 @@
 //     arithmetic of step 1, so the normalised values are never stored: the workspace holds
 //     only the sample and its prefix sums, at most 12 MiB whatever N and K.
 //  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans).
-//  4. k_prefix: running fp64 sums of the sorted values in the blocked order (blocks of
+//  4. k_prefix_*: running fp64 sums of the sorted values in the blocked order (blocks of
 //     kPrefixBlock values summed left to right from 0, the block offsets left to right over
 //     the block totals, then offset + block-local sum; the order fixes the rounding, which
 //     the codebook bits depend on).  One lane per block, so 1024 blocks run at once.
-//  5. k_lloyd: one wave runs Lloyd's iteration in fp64 from the mid-quantile start:
+//  5. k_lloyd: one workgroup runs Lloyd's iteration in fp64 from the mid-quantile start:
 //     thresholds (c_j + c_{j+1}) / 2, cell bounds by binary search over the sorted values,
 //     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
 //     codebook = (float)c.
@@ -291,52 +291,94 @@ __device__ __forceinline__ double prefix_pass(const uint32_t *__restrict__ keys,
 
 // P[0] = 0; P[i + 1] = off[b] + (s[b0] + ... + s[i]) for i in block b = [b0, b0 + 1024),
 // the block-local sum running left to right from 0 and off[b] = tot[0] + ... + tot[b - 1]
-// running left to right from 0 over the block totals.  Each lane runs its block's chain
-// twice (once for the total, once for the outputs) rather than storing and re-reading it.
-__global__ __launch_bounds__(kPrefixThreads) void k_prefix(const uint32_t *__restrict__ keys, int64_t S,
-                                                           double *__restrict__ P) {
-    __shared__ double tot[kPrefixThreads], offs[kPrefixThreads];
+// running left to right from 0 over the block totals.  Three launches, one lane per block
+// in one-wave workgroups (so the 1024 chains spread over 16 compute units instead of
+// sharing one): the block totals, parked in P[b0 + 1]; the offsets, which replace them
+// there; then each lane's outputs.  Each lane runs its block's chain twice (once for the
+// total, once for the outputs) rather than storing and re-reading it.  A block holds at
+// least one value, so P[b0 + 1] exists; only lane b reads or writes it in the last launch.
+constexpr int kPrefixWave = 64;
+__global__ __launch_bounds__(kPrefixWave) void k_prefix_tot(const uint32_t *__restrict__ keys, int64_t S,
+                                                            double *__restrict__ P) {
+    const int b = blockIdx.x * kPrefixWave + threadIdx.x;
+    const int nb = (int)((S + kPrefixBlock - 1) / kPrefixBlock);
+    if (b >= nb) return;
+    const int64_t b0 = (int64_t)b * kPrefixBlock;
+    const int64_t b1 = b0 + kPrefixBlock < S ? b0 + kPrefixBlock : S;
+    P[b0 + 1] = prefix_pass<false>(keys, b0, b1, 0.0, P);
+}
+
+__global__ __launch_bounds__(kPrefixThreads) void k_prefix_offs(int64_t S, double *__restrict__ P) {
+    __shared__ double tot[kPrefixThreads];
     const int t = threadIdx.x;
     const int nb = (int)((S + kPrefixBlock - 1) / kPrefixBlock);
-    const int64_t b0 = (int64_t)t * kPrefixBlock;
-    const int64_t b1 = b0 + kPrefixBlock < S ? b0 + kPrefixBlock : S;
-    if (t < nb) tot[t] = prefix_pass<false>(keys, b0, b1, 0.0, P);
+    if (t < nb) tot[t] = P[(int64_t)t * kPrefixBlock + 1];
     __syncthreads();
     if (t == 0) {
         double off = 0.0;
         for (int b = 0; b < nb; b++) {
-            offs[b] = off;
-            off = off + tot[b];
+            const double tb = tot[b];
+            tot[b] = off;
+            off = off + tb;
         }
-        P[0] = 0.0;
     }
     __syncthreads();
-    if (t < nb) prefix_pass<true>(keys, b0, b1, offs[t], P);
+    if (t < nb) P[(int64_t)t * kPrefixBlock + 1] = tot[t];
 }
 
-__device__ __forceinline__ int64_t count_le(const uint32_t *keys, int64_t S, double t) {
-    int64_t lo = 0, hi = S;
+__global__ __launch_bounds__(kPrefixWave) void k_prefix_write(const uint32_t *__restrict__ keys, int64_t S,
+                                                              double *__restrict__ P) {
+    const int b = blockIdx.x * kPrefixWave + threadIdx.x;
+    const int nb = (int)((S + kPrefixBlock - 1) / kPrefixBlock);
+    if (b >= nb) return;
+    const int64_t b0 = (int64_t)b * kPrefixBlock;
+    const int64_t b1 = b0 + kPrefixBlock < S ? b0 + kPrefixBlock : S;
+    const double off = P[b0 + 1];
+    if (b == 0) P[0] = 0.0;
+    prefix_pass<true>(keys, b0, b1, off, P);
+}
+
+// Lloyd's cell bounds: the number of sorted values <= t.  An LDS copy of every 32nd value
+// narrows the binary search to 32 values before it touches global memory (the count, and so
+// every bound, is the same as a search over all the values).
+constexpr int kIndexStride = 32;
+constexpr int kIndexMax = (int)(kSampleMax / kIndexStride);   // 128 KiB of fp32
+constexpr int kLloydThreads = 256;
+
+__device__ __forceinline__ int64_t count_le(const float *idx, int ni, const uint32_t *keys, int64_t S, double t) {
+    int lo = 0, hi = ni;
     while (lo < hi) {
-        const int64_t mid = lo + (hi - lo) / 2;
-        if ((double)key_to_f32(keys[mid]) <= t) lo = mid + 1; else hi = mid;
+        const int mid = (lo + hi) >> 1;
+        if ((double)idx[mid] <= t) lo = mid + 1; else hi = mid;
     }
-    return lo;
+    if (lo == 0) return 0;   // the smallest value is above t
+    // values 32 (lo - 1) and below are <= t; value 32 lo (if any) is above it
+    int64_t glo = (int64_t)(lo - 1) * kIndexStride + 1;
+    int64_t ghi = (int64_t)lo * kIndexStride < S ? (int64_t)lo * kIndexStride : S;
+    while (glo < ghi) {
+        const int64_t mid = glo + (ghi - glo) / 2;
+        if ((double)key_to_f32(keys[mid]) <= t) glo = mid + 1; else ghi = mid;
+    }
+    return glo;
 }
 
-__global__ __launch_bounds__(64) void k_lloyd(const uint32_t *__restrict__ keys,
-                                              const double *__restrict__ P, int64_t S,
-                                              float *__restrict__ cb) {
+__global__ __launch_bounds__(kLloydThreads) void k_lloyd(const uint32_t *__restrict__ keys,
+                                                         const double *__restrict__ P, int64_t S,
+                                                         float *__restrict__ cb) {
+    __shared__ float idx[kIndexMax];
     __shared__ double c[kLevels];
     __shared__ int64_t b[kLevels + 1], prev[kLevels + 1];
     __shared__ int changed;
     const int j = threadIdx.x;
+    const int ni = (int)((S + kIndexStride - 1) / kIndexStride);
+    for (int q = j; q < ni; q += kLloydThreads) idx[q] = key_to_f32(keys[(int64_t)q * kIndexStride]);
     if (j < kLevels) c[j] = (double)key_to_f32(keys[((int64_t)(2 * j + 1) * S) / 32]);
     if (j <= kLevels) prev[j] = -1;
     __syncthreads();
     int updates = 0;
     for (int pass = 0; pass <= kMaxUpdates; pass++) {
         if (j == 0) { b[0] = 0; b[kLevels] = S; changed = 0; }
-        if (j < kLevels - 1) b[j + 1] = count_le(keys, S, (c[j] + c[j + 1]) / 2.0);
+        if (j < kLevels - 1) b[j + 1] = count_le(idx, ni, keys, S, (c[j] + c[j + 1]) / 2.0);
         __syncthreads();
         if (j <= kLevels && b[j] != prev[j]) changed = 1;
         __syncthreads();
@@ -454,9 +496,14 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    hipLaunchKernelGGL(k_prefix, dim3(1), dim3(kPrefixThreads), 0, stream, keys, L.S, P);
+    const unsigned pblocks = (unsigned)((L.S + (int64_t)kPrefixBlock * kPrefixWave - 1) / ((int64_t)kPrefixBlock * kPrefixWave));
+    hipLaunchKernelGGL(k_prefix_tot, dim3(pblocks), dim3(kPrefixWave), 0, stream, keys, L.S, P);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lloyd, dim3(1), dim3(64), 0, stream, keys, P, L.S, cb);
+    hipLaunchKernelGGL(k_prefix_offs, dim3(1), dim3(kPrefixThreads), 0, stream, L.S, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_prefix_write, dim3(pblocks), dim3(kPrefixWave), 0, stream, keys, L.S, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_lloyd, dim3(1), dim3(kLloydThreads), 0, stream, keys, P, L.S, cb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (w_bf16)
         hipLaunchKernelGGL(k_assign_pack<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_ch, s_rel, cb,
