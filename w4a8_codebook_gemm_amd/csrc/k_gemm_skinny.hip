@@ -35,6 +35,12 @@
 //  * The codebook-pair table is the decode GEMV's (256 entries, 64 lane-private replicas).
 //    Up to 48 tokens the table reads of the next row tile are issued before the current
 //    tile's multiplies and MFMAs (scheduling barriers keep that order).
+//  * K split (w4a8_linear_ws, with a caller's workspace): where a CU would own few rows, K is
+//    cut into parts and each workgroup takes full row tiles over one part.  Each part
+//    stores its unscaled sums with device-scope relaxed atomic stores (written through to
+//    the point where every XCD sees them, without a cache-wide flush), then counts its
+//    arrival on the row block's counter; the last part to arrive reads every part's sums,
+//    adds them in part order and writes y, and the counter wraps back to zero.
 //  * Start-up: the epilogue's row and token scales, then the workgroup's group scales are
 //    requested before the first weight loads (a request behind them waits for them to drain
 //    from HBM); the group scales go straight to LDS through the buffer unit (16 B per lane),
