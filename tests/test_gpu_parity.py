@@ -171,6 +171,20 @@ def test_quantize_full_size(w, N, K):
     assert np.array_equal(L.packed.cpu().numpy(), q["packed"])
 
 
+def test_quantize_two_sampling_passes(w):
+    # more 256-blocks than one pass of the sampler's per-block buckets covers (2^19 - 1024
+    # blocks), so the fit sample is gathered in two passes over block ranges
+    N, K = 33280, 4096
+    say(f"quantize two sampling passes N={N} K={K}")
+    W = np.random.default_rng(7).standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+    q = O.quantize_weight(W, seed=3)
+    L = w.quantize_weight(gpu(W), seed=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(L.codebook.cpu().numpy().view(np.uint32), q["cb"].view(np.uint32))
+    assert np.array_equal(L.s_rel.cpu().numpy(), q["s_rel"])
+    assert np.array_equal(L.packed.cpu().numpy(), q["packed"])
+
+
 # ----------------------------------------------------------------------------- linear
 
 def run_linear(w, algo, N, K, M, rows=None, toks=None, out_dtype=torch.float32, seed=0, n_out=None):

@@ -205,6 +205,119 @@ __global__ __launch_bounds__(64 * kSampleWaves) void k_sample_keys(
     for (int64_t i = S + t; i < P2; i += nthreads) keys[i] = 0xFFFFFFFFu;
 }
 
+// Sampled fits (N*K > 2^20) by block: k_sample_keys rotates a whole 256-block for every
+// sample, about three times per block at the MLP shapes.  These kernels rotate each block
+// that holds samples once instead.  For a chunk of kChunkBlocks 256-blocks at a time they
+// count the samples per block, turn the counts into offsets, list each block's sample
+// indices (in any order) and let one wave per block rotate it and write keys[i] for each
+// of its samples i -- the same keys at the same places as k_sample_keys writes.  The counts,
+// cursors and list live in the prefix-sum area of the workspace, unused until the sort is
+// done.
+constexpr int64_t kChunkBlocks = (1 << 19) - 1024;   // with the scratch below, fills the prefix area
+constexpr int kCountThreads = 256;
+
+__device__ __forceinline__ int64_t sample_pos(uint64_t seed, int64_t i, int64_t NK) {
+    return (int64_t)__umul64hi(splitmix64_at(seed, (uint64_t)i), (uint64_t)NK);
+}
+
+__global__ __launch_bounds__(kCountThreads) void k_fill_u32(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = t; i < n; i += stride) p[i] = v;
+}
+
+__global__ __launch_bounds__(kCountThreads) void k_sample_count(uint64_t seed, int64_t S, int64_t NK, int64_t c0,
+                                                                int64_t c1, uint32_t *__restrict__ cnt) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= S) return;
+    const int64_t blk = sample_pos(seed, i, NK) / kRot;
+    if (blk >= c0 && blk < c1) atomicAdd(&cnt[blk - c0], 1u);
+}
+
+// cnt[0 .. n) -> exclusive offsets (integers: exact in any order), cnt[n] = total; cur = a
+// copy of the offsets.  Segments of 1024 counts: each workgroup scans its own in LDS and
+// records the segment's total; then each adds the totals of the segments before it.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_sample_scan_seg(uint32_t *__restrict__ cnt, int64_t n,
+                                                                  uint32_t *__restrict__ segsum) {
+    __shared__ uint32_t sh[kScanThreads];
+    const int t = threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * kScanThreads + t;
+    const uint32_t v = i < n ? cnt[i] : 0u;
+    sh[t] = v;
+    __syncthreads();
+    for (int d = 1; d < kScanThreads; d <<= 1) {
+        const uint32_t x = t >= d ? sh[t - d] : 0u;
+        __syncthreads();
+        sh[t] += x;
+        __syncthreads();
+    }
+    if (i < n) cnt[i] = sh[t] - v;
+    if (t == kScanThreads - 1) segsum[blockIdx.x] = sh[t];
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_sample_scan_add(uint32_t *__restrict__ cnt, uint32_t *__restrict__ cur,
+                                                                  int64_t n, const uint32_t *__restrict__ segsum) {
+    __shared__ uint32_t base;
+    const int t = threadIdx.x;
+    const int seg = blockIdx.x;
+    if (t == 0) base = 0u;
+    __syncthreads();
+    for (int q = t; q < seg; q += kScanThreads) atomicAdd(&base, segsum[q]);
+    __syncthreads();
+    const uint32_t b = base;
+    const int64_t i = (int64_t)seg * kScanThreads + t;
+    if (i < n) {
+        const uint32_t c = cnt[i] + b;
+        cnt[i] = c;
+        cur[i] = c;
+    }
+    if (seg == (int)gridDim.x - 1 && t == 0) cnt[n] = b + segsum[seg];
+}
+
+__global__ __launch_bounds__(kCountThreads) void k_sample_list(uint64_t seed, int64_t S, int64_t NK, int64_t c0,
+                                                               int64_t c1, uint32_t *__restrict__ cur,
+                                                               uint32_t *__restrict__ list) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= S) return;
+    const int64_t blk = sample_pos(seed, i, NK) / kRot;
+    if (blk >= c0 && blk < c1) list[atomicAdd(&cur[blk - c0], 1u)] = (uint32_t)i;
+}
+
+// One wave per block of the chunk: rotate and normalise it as k_sample_keys does, then
+// write the key of each sample it holds.  The block's loads go out before its sample count
+// is known; lane t takes the block's t-th listed sample and fetches its value from the lane
+// that holds it (up to 64 samples at a time).
+template <bool BF16>
+__global__ __launch_bounds__(64 * kSampleWaves) void k_sample_blocks(
+    const void *__restrict__ w, int64_t K, int64_t NK, uint64_t seed, int64_t c0, int64_t c1,
+    const float *__restrict__ s_ch, const uint8_t *__restrict__ s_rel, const uint32_t *__restrict__ cnt,
+    const uint32_t *__restrict__ list, uint32_t *__restrict__ keys) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = c0 + (int64_t)blockIdx.x * kSampleWaves + (threadIdx.x >> 6);
+    if (blk >= c1) return;
+    const int64_t pos0 = blk * kRot, r = pos0 / K, blk0 = pos0 - r * K;
+    float v[4];
+    load4<BF16>(w, pos0 + 4 * lane, v);
+    const uint32_t code = s_rel[r * (K / kGroup) + blk0 / kGroup + (lane >> 2)];
+    const float rmax = s_ch[r];
+    const uint32_t q0 = cnt[blk - c0], q1 = cnt[blk - c0 + 1];
+    if (q0 == q1) return;
+    fwht256_lane4(v, lane);
+    normalise4(v, rmax, code);
+    for (uint32_t qb = q0; qb < q1; qb += 64) {
+        const uint32_t q = qb + (uint32_t)lane;
+        const bool mine = q < q1;
+        const int64_t i = mine ? (int64_t)list[q] : 0;
+        const int e = mine ? (int)(sample_pos(seed, i, NK) - pos0) : 0;   // the sample's element
+        const int src = e >> 2;
+        const float a0 = __shfl(v[0], src), a1 = __shfl(v[1], src), a2 = __shfl(v[2], src), a3 = __shfl(v[3], src);
+        const int c = e & 3;
+        const float val = c == 0 ? a0 : c == 1 ? a1 : c == 2 ? a2 : a3;
+        if (mine) keys[i] = f32_to_key(val);
+    }
+}
+
 // Bitonic network: pass (k, j) compares i with i ^ j, ascending where (i & k) == 0.
 __device__ __forceinline__ void cmp_swap(uint32_t &x, uint32_t &y, bool asc) {
     if ((x > y) == asc) {
@@ -472,15 +585,52 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
         hipLaunchKernelGGL(k_rotate_scale<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_rel, s_ch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    const int64_t jobs = NK > kSampleMax ? L.S : NK / kRot;
-    const unsigned sblocks = (unsigned)((jobs + kSampleWaves - 1) / kSampleWaves);
-    if (w_bf16)
-        hipLaunchKernelGGL(k_sample_keys<true>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
-                           L.P2, seed, s_ch, s_rel, keys);
-    else
-        hipLaunchKernelGGL(k_sample_keys<false>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
-                           L.P2, seed, s_ch, s_rel, keys);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (NK > kSampleMax) {
+        // S = 2^20 = P2: no padding.  Counts, cursors and the list in the prefix-sum area.
+        static_assert(round256((kChunkBlocks + 1) * 4) + kChunkBlocks * 4 + kSampleMax * 4 +
+                              4 * ((kChunkBlocks + kScanThreads - 1) / kScanThreads) <=
+                          round256((kSampleMax + 1) * 8),
+                      "sampling scratch inside the prefix area");
+        uint32_t *cnt = reinterpret_cast<uint32_t *>(P);
+        uint32_t *cur = cnt + round256((kChunkBlocks + 1) * 4) / 4;
+        uint32_t *list = cur + kChunkBlocks;
+        uint32_t *segsum = list + kSampleMax;
+        const int64_t nb = NK / kRot;
+        const unsigned cgrid = (unsigned)((L.S + kCountThreads - 1) / kCountThreads);
+        for (int64_t c0 = 0; c0 < nb; c0 += kChunkBlocks) {
+            const int64_t c1 = c0 + kChunkBlocks < nb ? c0 + kChunkBlocks : nb;
+            hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(kCountThreads), 0, stream, cnt, c1 - c0 + 1, 0u);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_sample_count, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cnt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const unsigned nseg = (unsigned)((c1 - c0 + kScanThreads - 1) / kScanThreads);
+            hipLaunchKernelGGL(k_sample_scan_seg, dim3(nseg), dim3(kScanThreads), 0, stream, cnt, c1 - c0, segsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_sample_scan_add, dim3(nseg), dim3(kScanThreads), 0, stream, cnt, cur, c1 - c0, segsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_sample_list, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cur,
+                               list);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            const unsigned bgrid = (unsigned)((c1 - c0 + kSampleWaves - 1) / kSampleWaves);
+            if (w_bf16)
+                hipLaunchKernelGGL(k_sample_blocks<true>, dim3(bgrid), dim3(64 * kSampleWaves), 0, stream, w, K, NK,
+                                   seed, c0, c1, s_ch, s_rel, cnt, list, keys);
+            else
+                hipLaunchKernelGGL(k_sample_blocks<false>, dim3(bgrid), dim3(64 * kSampleWaves), 0, stream, w, K, NK,
+                                   seed, c0, c1, s_ch, s_rel, cnt, list, keys);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    } else {
+        const int64_t jobs = NK / kRot;
+        const unsigned sblocks = (unsigned)((jobs + kSampleWaves - 1) / kSampleWaves);
+        if (w_bf16)
+            hipLaunchKernelGGL(k_sample_keys<true>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
+                               L.P2, seed, s_ch, s_rel, keys);
+        else
+            hipLaunchKernelGGL(k_sample_keys<false>, dim3(sblocks), dim3(64 * kSampleWaves), 0, stream, w, K, NK, L.S,
+                               L.P2, seed, s_ch, s_rel, keys);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
 
     const unsigned tiles = (unsigned)(L.P2 / kSortTile);
     hipLaunchKernelGGL(k_bitonic_tile, dim3(tiles), dim3(kSortTile / 2), 0, stream, keys, (int64_t)2,
