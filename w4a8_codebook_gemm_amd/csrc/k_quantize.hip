@@ -451,28 +451,47 @@ __global__ __launch_bounds__(kPrefixWave) void k_prefix_write(const uint32_t *__
     prefix_pass<true>(keys, b0, b1, off, P);
 }
 
-// Lloyd's cell bounds: the number of sorted values <= t.  An LDS copy of every 32nd value
-// narrows the binary search to 32 values before it touches global memory (the count, and so
-// every bound, is the same as a search over all the values).
+// Lloyd's cell bounds: the number of sorted values <= t, found by the 16 lanes of one
+// group per threshold.  A 16-way search over an LDS copy of every 32nd value (each lane
+// tests one of 16 evenly spaced entries; the group's ballot tells which sixteenth holds the
+// boundary) finds the 32-value window that holds it; the window (one 128-byte line, two
+// values per lane) is then counted by a ballot.  The count, and so every bound, is the one
+// a search over all the values gives.
 constexpr int kIndexStride = 32;
 constexpr int kIndexMax = (int)(kSampleMax / kIndexStride);   // 128 KiB of fp32
-constexpr int kLloydThreads = 256;
+constexpr int kLloydThreads = 256;                              // 16 lanes per threshold
 
-__device__ __forceinline__ int64_t count_le(const float *idx, int ni, const uint32_t *keys, int64_t S, double t) {
+__device__ __forceinline__ uint32_t group16_count(bool pred, int lane) {
+    const unsigned long long m = __ballot(pred);
+    return (uint32_t)__popcll((m >> (16 * (lane >> 4))) & 0xFFFFull);
+}
+
+__device__ __forceinline__ int64_t count_le16(const float *idx, int ni, const uint32_t *keys, int64_t S, double t,
+                                              int lane) {
+    const int sl = lane & 15;
+    // c = #{entries <= t} stays in [lo, hi]
     int lo = 0, hi = ni;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if ((double)idx[mid] <= t) lo = mid + 1; else hi = mid;
+    while (lo < hi) {   // the same bounds in all 16 lanes of the group
+        const int n = hi - lo;
+        const int p = lo + (int)(((int64_t)(sl + 1) * n + 15) / 16) - 1;   // lo <= p <= hi - 1
+        const uint32_t k = group16_count((double)idx[p] <= t, lane);
+        const int pk1 = lo + (int)(((int64_t)k * n + 15) / 16) - 1;        // pivot k - 1
+        const int pk = lo + (int)(((int64_t)(k + 1) * n + 15) / 16) - 1;   // pivot k
+        if (k == 0) {
+            hi = pk;
+        } else {
+            lo = pk1 + 1;
+            if (k < 16) hi = pk;
+        }
     }
     if (lo == 0) return 0;   // the smallest value is above t
-    // values 32 (lo - 1) and below are <= t; value 32 lo (if any) is above it
-    int64_t glo = (int64_t)(lo - 1) * kIndexStride + 1;
-    int64_t ghi = (int64_t)lo * kIndexStride < S ? (int64_t)lo * kIndexStride : S;
-    while (glo < ghi) {
-        const int64_t mid = glo + (ghi - glo) / 2;
-        if ((double)key_to_f32(keys[mid]) <= t) glo = mid + 1; else ghi = mid;
-    }
-    return glo;
+    // values before 32 (lo - 1) are <= t and values from 32 lo on (if any) above it; the
+    // window [32 (lo - 1), 32 lo) lies inside the keys, whose length is a multiple of 32
+    const int64_t base = (int64_t)(lo - 1) * kIndexStride;
+    const uint2 w2 = reinterpret_cast<const uint2 *>(keys + base)[sl];
+    const bool p0 = base + 2 * sl < S && (double)key_to_f32(w2.x) <= t;
+    const bool p1 = base + 2 * sl + 1 < S && (double)key_to_f32(w2.y) <= t;
+    return base + group16_count(p0, lane) + group16_count(p1, lane);
 }
 
 __global__ __launch_bounds__(kLloydThreads) void k_lloyd(const uint32_t *__restrict__ keys,
@@ -491,7 +510,12 @@ __global__ __launch_bounds__(kLloydThreads) void k_lloyd(const uint32_t *__restr
     int updates = 0;
     for (int pass = 0; pass <= kMaxUpdates; pass++) {
         if (j == 0) { b[0] = 0; b[kLevels] = S; changed = 0; }
-        if (j < kLevels - 1) b[j + 1] = count_le(idx, ni, keys, S, (c[j] + c[j + 1]) / 2.0);
+        {
+            // group g = j / 16 searches threshold g (group 15 repeats threshold 14 and drops it)
+            const int g = j >> 4, gt = g < kLevels - 1 ? g : kLevels - 2;
+            const int64_t n = count_le16(idx, ni, keys, S, (c[gt] + c[gt + 1]) / 2.0, j & 63);
+            if (g < kLevels - 1 && (j & 15) == 0) b[g + 1] = n;
+        }
         __syncthreads();
         if (j <= kLevels && b[j] != prev[j]) changed = 1;
         __syncthreads();
