@@ -337,6 +337,49 @@ __global__ void k_bitonic_global(uint32_t *keys, int64_t k, int64_t j) {
     keys[l] = y;
 }
 
+// Passes (k, j) and (k, j / 2) in one sweep: thread t owns i (bits j and j / 2 clear) and
+// i + j / 2, i + j, i + 3 j / 2, which those two passes compare only among themselves, all
+// in one direction (k > j).
+__global__ void k_bitonic_global2(uint32_t *keys, int64_t k, int64_t j) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t h = j >> 1;
+    const int64_t i = (t / h) * 2 * j + (t % h);
+    uint32_t a = keys[i], b = keys[i + h], c = keys[i + j], d = keys[i + j + h];
+    const bool asc = (i & k) == 0;
+    cmp_swap(a, c, asc);
+    cmp_swap(b, d, asc);
+    cmp_swap(a, b, asc);
+    cmp_swap(c, d, asc);
+    keys[i] = a;
+    keys[i + h] = b;
+    keys[i + j] = c;
+    keys[i + j + h] = d;
+}
+
+// Passes (k, j), (k, j / 2) and (k, j / 4) in one sweep: thread t owns the eight elements
+// i + m j / 4 (m = 0 .. 7, i with bits j, j / 2, j / 4 clear), which those passes compare
+// only among themselves.
+__global__ void k_bitonic_global3(uint32_t *keys, int64_t k, int64_t j) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t q = j >> 2;
+    const int64_t i = (t / q) * 2 * j + (t % q);
+    uint32_t x[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) x[m] = keys[i + m * q];
+    const bool asc = (i & k) == 0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) cmp_swap(x[m], x[m + 4], asc);
+#pragma unroll
+    for (int m = 0; m < 8; m += 4) {
+        cmp_swap(x[m], x[m + 2], asc);
+        cmp_swap(x[m + 1], x[m + 3], asc);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; m += 2) cmp_swap(x[m], x[m + 1], asc);
+#pragma unroll
+    for (int m = 0; m < 8; m++) keys[i + m * q] = x[m];
+}
+
 // All passes with j < kSortTile for one k (k_from == k_to), or the whole sort of every
 // tile up to k = kSortTile (k_from = 2, k_to = kSortTile), inside one LDS tile.
 __global__ __launch_bounds__(kSortTile / 2) void k_bitonic_tile(uint32_t *keys, int64_t k_from,
@@ -661,9 +704,17 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
                        (int64_t)kSortTile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     for (int64_t k = 2 * kSortTile; k <= L.P2; k <<= 1) {
-        for (int64_t j = k >> 1; j >= kSortTile; j >>= 1) {  // spans the tiles cannot hold
-            const int64_t pairs = L.P2 / 2;
-            hipLaunchKernelGGL(k_bitonic_global, dim3((unsigned)(pairs / 256)), dim3(256), 0, stream, keys, k, j);
+        for (int64_t j = k >> 1; j >= kSortTile;) {  // spans the tiles cannot hold, up to three at a time
+            if ((j >> 2) >= kSortTile) {
+                hipLaunchKernelGGL(k_bitonic_global3, dim3((unsigned)(L.P2 / 8 / 256)), dim3(256), 0, stream, keys, k, j);
+                j >>= 3;
+            } else if ((j >> 1) >= kSortTile) {
+                hipLaunchKernelGGL(k_bitonic_global2, dim3((unsigned)(L.P2 / 4 / 256)), dim3(256), 0, stream, keys, k, j);
+                j >>= 2;
+            } else {
+                hipLaunchKernelGGL(k_bitonic_global, dim3((unsigned)(L.P2 / 2 / 256)), dim3(256), 0, stream, keys, k, j);
+                j >>= 1;
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         hipLaunchKernelGGL(k_bitonic_tile, dim3(tiles), dim3(kSortTile / 2), 0, stream, keys, k, k);
