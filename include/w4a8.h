@@ -287,9 +287,11 @@ typedef struct {
  * input, or gate and up) in one call [card "...w4a8-convrot-ComfyUI", section "Why this
  * exists": decode re-reads every weight for every token, so each launch's fixed cost is paid
  * once per layer per token].  Where w4a8_linear takes the GEMV (M <= 3 and M*K <= 40960)
- * all layers run in ONE launch, its workgroups split between the layers in proportion to their rows; otherwise
- * each layer runs as w4a8_linear would.  Every y is bit-identical to what w4a8_linear gives
- * for that layer alone.
+ * all layers run in ONE launch, its workgroups split between the layers in proportion to their rows.
+ * Where it takes the batched-decode kernel and all layers have the same N, they also run in
+ * one launch, each workgroup doing what the single-layer launch does for its rows.
+ * Otherwise each layer runs as w4a8_linear would.  Every y is bit-identical to what
+ * w4a8_linear gives for that layer alone.
  *
  *  layers   HOST array of G descriptors, 1 <= G <= 8; read during the call only
  *  others   as for w4a8_linear; each layer is validated like a w4a8_linear call

@@ -69,6 +69,32 @@ def test_linear_multi_matches_single(w, M, K, G):
     assert np.all(err <= 4e-3 * A)
 
 
+@pytest.mark.parametrize("M,K,G,N,dt", [(8, 5120, 4, 5120, "f32"), (40, 1024, 3, 1000, "bf16"), (4, 2048, 2, 77, "f32"),
+                                        (64, 512, 8, 300, "f32"), (17, 8192, 2, 5120, "bf16")])
+def test_linear_multi_same_rows_one_launch(w, M, K, G, N, dt):
+    # layers with one row count run as one batched-decode launch; each output must match
+    # the single-layer call bit for bit
+    say(f"linear_multi same N={N} M={M} K={K} G={G} {dt}")
+    qs = [oracle_layer(N, K, 40 + g) for g in range(G)]
+    Ls = [w.QuantizedLinear(gpu(q["packed"]), gpu(q["s_rel"]), gpu(q["s_ch"]), gpu(q["cb"])) for q in qs]
+    x = S.activations(M, K, seed=7 * M + K, n_outliers=2)
+    xq, sx = O.prepare(x)
+    xg, sg = gpu(xq), gpu(sx)
+    odt = torch.bfloat16 if dt == "bf16" else torch.float32
+    assert w.linear_pick(M, N, K) == w.ALGO_MFMA_SKINNY
+    ys = w.linear_multi(xg, sg, Ls, out_dtype=odt)
+    ref = [w.linear(xg, sg, L, out_dtype=odt) for L in Ls]
+    torch.cuda.synchronize()
+    for g in range(G):
+        assert torch.equal(ys[g], ref[g]), g
+    # the last layer against the oracle as well
+    q = qs[-1]
+    yr, A = O.linear_ref(xq, sx, q["packed"], q["s_rel"], q["s_ch"], q["cb"])
+    err = np.abs(ys[-1].float().cpu().numpy().astype(np.float64) - yr)
+    bound = 4e-3 * A + (np.abs(yr) * 2.0 ** -8 if dt == "bf16" else 0.0)
+    assert np.all(err <= bound)
+
+
 @pytest.mark.parametrize("M,K,G,dt", [(1, 5120, 4, "f32"), (1, 17408, 2, "bf16"), (2, 5120, 3, "f32"),
                                       (2, 1024, 8, "bf16"), (1, 33024, 2, "f32"), (3, 512, 2, "f32")])
 def test_forward_multi_matches_single(w, M, K, G, dt):

@@ -221,6 +221,19 @@ int w4a8_linear_multi(const int8_t *x_q, const float *s_x, int64_t M, int64_t K,
     int st = check_multi(x_q, s_x, M, K, G, layers, y_dtype, d);
     if (st != W4A8_OK) return st;
     if (!gemv_auto(M, K)) {
+        // layers of one row count on the batched-decode kernel: one launch, each workgroup
+        // running what the single-layer launch runs for its rows
+        bool same_n = G > 1;
+        for (int g = 1; g < G; g++) same_n = same_n && d[g].N == d[0].N;
+        if (same_n && pick(M, d[0].N, K) == W4A8_ALGO_MFMA_SKINNY) {
+            int num_cu = 0;
+            st = current_device(&num_cu);
+            if (st != W4A8_OK) return st;
+            w4a8::LinearArgs a{x_q, s_x, M, K, d[0].N, d[0].packed, d[0].s_rel, d[0].s_ch, d[0].cb, d[0].y,
+                               y_dtype == W4A8_BF16, nullptr, 0, nullptr, nullptr};
+            hipError_t e = w4a8::launch_gemm_skinny_multi(a, d, G, num_cu, static_cast<hipStream_t>(stream));
+            return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+        }
         for (int g = 0; g < G; g++) {
             st = w4a8_linear(x_q, s_x, M, K, d[g].packed, d[g].s_rel, d[g].s_ch, d[g].cb, d[g].N, d[g].y,
                              y_dtype, stream);

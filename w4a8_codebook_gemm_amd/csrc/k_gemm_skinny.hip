@@ -96,8 +96,15 @@ __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &
     hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias);
 }
 
+// Layers of one launch (all with the same N): layer g owns workgroups [g nrb, (g + 1) nrb),
+// each running exactly what the single-layer launch runs for its row block.
+struct SkinnyTab {
+    int G, nrb;
+    LayerDesc L[kMaxGroup];
+};
+
 template <int NT, int MT16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg) {
+__global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg, SkinnyTab lt) {
     static_assert(WAVES * NT <= kSmemBytes / 1024, "reduction buffer");
     // pair table (later the wave reduction) in static LDS, whose address folds into every
     // table read; the staged group scales in the dynamic part
@@ -109,8 +116,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_skinny(LinearArgs a, int rows_wg
     const int li = lane & 15, lq = lane >> 4;
     const int64_t M = a.M, N = a.N, K = a.K;
     // with a split of K, workgroup b takes part ks = b % ksplit of K for row block b / ksplit
+    int bid = (int)blockIdx.x;
+    if (lt.G > 1) {
+        // this workgroup's layer (compile-time indices keep the table in kernel arguments)
+        const int g = bid / lt.nrb;
+        bid -= g * lt.nrb;
+#pragma unroll
+        for (int q = 0; q < kMaxGroup; q++)
+            if (q == g) {
+                a.packed = lt.L[q].packed;
+                a.s_rel = lt.L[q].s_rel;
+                a.s_ch = lt.L[q].s_ch;
+                a.cb = lt.L[q].cb;
+                a.y = lt.L[q].y;
+            }
+    }
     const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
-    const int ks = (int)(blockIdx.x % (unsigned)ksplit), rb = (int)(blockIdx.x / (unsigned)ksplit);
+    const int ks = bid % ksplit, rb = bid / ksplit;
     const int64_t r_begin = (int64_t)rb * rows_wg;
     const int nrows = (int)min((int64_t)rows_wg, N - r_begin);
     const uint32_t rowbytes = (uint32_t)(K / 2), grpbytes = (uint32_t)(K / kGroup);
@@ -410,7 +432,7 @@ template <int NT, int MT16>
 constexpr int waves_for() { return (MT16 == 1 && NT <= 3) ? 16 : (MT16 <= 2 ? 8 : 4); }
 
 template <int NT, int MT16>
-hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
+hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, const SkinnyTab &tab, hipStream_t stream) {
     constexpr int W = waves_for<NT, MT16>();
     const int64_t lds = skinny_scale_bytes(rows_wg, a.K / kGroup / (a.ksplit > 1 ? a.ksplit : 1));
     // set once per kernel instance; concurrent first calls may both set it, which is harmless
@@ -421,17 +443,17 @@ hipError_t launch_one(const LinearArgs &a, unsigned grid, int rows_wg, hipStream
         if (e != hipSuccess) return e;
         attr_set.store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a, rows_wg);
+    hipLaunchKernelGGL((k_skinny<NT, MT16, W>), dim3(grid), dim3(64 * W), (size_t)lds, stream, a, rows_wg, tab);
     return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_nt(const LinearArgs &a, unsigned grid, int rows_wg, hipStream_t stream) {
+hipError_t launch_nt(const LinearArgs &a, unsigned grid, int rows_wg, const SkinnyTab &tab, hipStream_t stream) {
     switch ((a.M + 15) / 16) {
-        case 1: return launch_one<NT, 1>(a, grid, rows_wg, stream);
-        case 2: return launch_one<NT, 2>(a, grid, rows_wg, stream);
-        case 3: return launch_one<NT, 3>(a, grid, rows_wg, stream);
-        case 4: return launch_one<NT, 4>(a, grid, rows_wg, stream);
+        case 1: return launch_one<NT, 1>(a, grid, rows_wg, tab, stream);
+        case 2: return launch_one<NT, 2>(a, grid, rows_wg, tab, stream);
+        case 3: return launch_one<NT, 3>(a, grid, rows_wg, tab, stream);
+        case 4: return launch_one<NT, 4>(a, grid, rows_wg, tab, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -471,8 +493,12 @@ int64_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int num_cu) {
     return q == 1 ? 0 : kSkinnyCounterBytes + (int64_t)q * M * N * 4;
 }
 
-hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
-    if (!skinny_supported(a.M, a.N, a.K)) return hipErrorInvalidValue;
+namespace {
+
+// One launch of G layers of N rows each (G = 1: the layer in a).
+hipError_t launch_skinny_layers(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu, hipStream_t stream) {
+    if (!skinny_supported(a.M, a.N, a.K) || G < 1 || G > kMaxGroup) return hipErrorInvalidValue;
+    if (G > 1 && a.ksplit > 1) return hipErrorInvalidValue;
     const int q = a.ksplit > 1 ? a.ksplit : 1;
     if (q > 1 && (a.K % (256 * q) != 0 || !a.ws_part || !a.ws_cnt)) return hipErrorInvalidValue;
     // rows per workgroup: an equal share for every CU (per part of K), at most kMaxTiles
@@ -482,14 +508,32 @@ hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t strea
     while (rows > 16 && kSmemBytes + skinny_scale_bytes(rows, a.K / kGroup / q) > kSkinnyLdsMax) rows -= 16;
     if (rows < 1) rows = 1;
     const int64_t nt = (rows + 15) / 16;
-    const unsigned grid = (unsigned)(((a.N + rows - 1) / rows) * q);
+    const int64_t nrb = ((a.N + rows - 1) / rows) * q;   // workgroups per layer
+    SkinnyTab tab{};
+    tab.G = G;
+    tab.nrb = (int)nrb;
+    for (int g = 0; g < G && layers; g++) tab.L[g] = layers[g];
+    const unsigned grid = (unsigned)(nrb * G);
     switch (nt) {
-        case 1: return launch_nt<1>(a, grid, (int)rows, stream);
-        case 2: return launch_nt<2>(a, grid, (int)rows, stream);
-        case 3: return launch_nt<3>(a, grid, (int)rows, stream);
-        case 4: return launch_nt<4>(a, grid, (int)rows, stream);
-        default: return launch_nt<5>(a, grid, (int)rows, stream);
+        case 1: return launch_nt<1>(a, grid, (int)rows, tab, stream);
+        case 2: return launch_nt<2>(a, grid, (int)rows, tab, stream);
+        case 3: return launch_nt<3>(a, grid, (int)rows, tab, stream);
+        case 4: return launch_nt<4>(a, grid, (int)rows, tab, stream);
+        default: return launch_nt<5>(a, grid, (int)rows, tab, stream);
     }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream) {
+    return launch_skinny_layers(a, nullptr, 1, num_cu, stream);
+}
+
+hipError_t launch_gemm_skinny_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                                    hipStream_t stream) {
+    for (int g = 0; g < G; g++)
+        if (layers[g].N != a.N) return hipErrorInvalidValue;
+    return launch_skinny_layers(a, layers, G, num_cu, stream);
 }
 
 }  // namespace w4a8

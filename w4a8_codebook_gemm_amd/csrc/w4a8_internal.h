@@ -318,6 +318,10 @@ constexpr int64_t kSkinnyCounterBytes = 4096;  // the split's arrival counters: 
 int skinny_split(int64_t M, int64_t N, int64_t K, int num_cu);
 int64_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int num_cu);
 hipError_t launch_gemm_skinny(const LinearArgs &a, int num_cu, hipStream_t stream);
+// G layers of a.N rows each in one launch (no K split), every output bit-identical to the
+// single-layer launch's
+hipError_t launch_gemm_skinny_multi(const LinearArgs &a, const LayerDesc *layers, int G, int num_cu,
+                                    hipStream_t stream);
 
 // W8A8 comparator (per-row int8 weights of the rotated rows, no codebook)
 struct W8Args {
