@@ -27,8 +27,8 @@
 //     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
 //     codebook = (float)c.
 //  6. k_assign_pack: per row, rotate and normalise again (the arithmetic of steps 1 and 2),
-//     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 }, two indices per
-//     byte, even element in the low nibble.
+//     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 } (decided by an
+//     equivalent fp32 compare), two indices per byte, even element in the low nibble.
 #include <atomic>
 
 #include "w4a8_internal.h"
@@ -582,9 +582,16 @@ __global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict
                                                           const uint8_t *__restrict__ s_rel,
                                                           const float *__restrict__ cb,
                                                           int8_t *__restrict__ packed) {
-    __shared__ double mid[kLevels - 1];
-    if (threadIdx.x < kLevels - 1)
-        mid[threadIdx.x] = ((double)cb[threadIdx.x] + (double)cb[threadIdx.x + 1]) / 2.0;
+    // each midpoint (cb[j] + cb[j+1]) / 2, exact in fp64, as the largest fp32 at or below it:
+    // for an fp32 v, (double)v > mid exactly when v > that fp32, so one fp32 compare per
+    // level decides what the fp64 compare decides
+    __shared__ float thr[kLevels - 1];
+    if (threadIdx.x < kLevels - 1) {
+        const double m = ((double)cb[threadIdx.x] + (double)cb[threadIdx.x + 1]) / 2.0;
+        float f = (float)m;
+        if ((double)f > m) f = nextafterf(f, -INFINITY);
+        thr[threadIdx.x] = f;
+    }
     __syncthreads();
     const int64_t r = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict
 #pragma unroll
         for (int j = 0; j < kLevels - 1; j++)
 #pragma unroll
-            for (int q = 0; q < 4; q++) idx[q] += ((double)v[q] > mid[j]) ? 1 : 0;
+            for (int q = 0; q < 4; q++) idx[q] += (v[q] > thr[j]) ? 1 : 0;
         const uint16_t two = (uint16_t)((idx[0] | (idx[1] << 4)) | ((idx[2] | (idx[3] << 4)) << 8));
         *reinterpret_cast<uint16_t *>(packed + r * (K / 2) + (int64_t)b * (kRot / 2) + 2 * lane) = two;
     }
