@@ -124,6 +124,20 @@ int main(void) {
     EXPECT(w4a8_forward_multi(MIS, 0, 1, 512, 2, t, 0, FAKE, FAKE, NULL), W4A8_ERR_ALIGN);
     EXPECT(w4a8_forward_multi(FAKE, 0, 1, 512, 2, t, 0, NULL, FAKE, NULL), W4A8_ERR_NULL);
 
+    /* the product with a workspace (checks that return before any device call) */
+    EXPECT(w4a8_linear_workspace_bytes(8, 256, 300), -W4A8_ERR_SHAPE);
+    EXPECT(w4a8_linear_workspace_bytes(0, 256, 512), -W4A8_ERR_SHAPE);
+    EXPECT(w4a8_linear_workspace_bytes(1, 17408, 5120), 0);     /* the GEMV: no workspace */
+    EXPECT(w4a8_linear_workspace_bytes(2048, 5120, 17408), 0);  /* prefill: no workspace */
+    EXPECT(w4a8_linear_ws(NULL, FAKE, 32, 8192, FAKE, FAKE, FAKE, FAKE, 5120, FAKE, 0, FAKE, 1 << 20, NULL),
+           W4A8_ERR_NULL);
+    EXPECT(w4a8_linear_ws(FAKE, FAKE, 32, 8200, FAKE, FAKE, FAKE, FAKE, 5120, FAKE, 0, FAKE, 1 << 20, NULL),
+           W4A8_ERR_SHAPE);
+    EXPECT(w4a8_linear_ws(FAKE, FAKE, 32, 8192, FAKE, FAKE, FAKE, FAKE, 5120, FAKE, 7, FAKE, 1 << 20, NULL),
+           W4A8_ERR_DTYPE);
+    EXPECT(w4a8_linear_ws(FAKE, FAKE, 32, 8192, FAKE, FAKE, FAKE, FAKE, 5120, FAKE, 0, MIS, 1 << 20, NULL),
+           W4A8_ERR_ALIGN);
+
     /* the W8A8 comparator */
     EXPECT(w4a8_w8a8_quantize_weight(NULL, 0, 8, 256, FAKE, FAKE, NULL), W4A8_ERR_NULL);
     EXPECT(w4a8_w8a8_quantize_weight(FAKE, 0, 8, 131072 + 256, FAKE, FAKE, NULL), W4A8_ERR_SHAPE);
