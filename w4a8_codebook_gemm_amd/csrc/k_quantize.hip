@@ -602,11 +602,13 @@ __global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict
         load4<BF16>(w, r * K + (int64_t)b * kRot + 4 * lane, v);
         fwht256_lane4(v, lane);
         normalise4(v, rmax, s_rel[r * (K / kGroup) + b * 16 + (lane >> 2)]);
+        // the number of thresholds below v, by a four-step binary search over the ascending
+        // thresholds (the same count as comparing with all fifteen)
         int idx[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < kLevels - 1; j++)
+        for (int step = 8; step >= 1; step >>= 1)
 #pragma unroll
-            for (int q = 0; q < 4; q++) idx[q] += (v[q] > thr[j]) ? 1 : 0;
+            for (int q = 0; q < 4; q++) idx[q] += (v[q] > thr[idx[q] + step - 1]) ? step : 0;
         const uint16_t two = (uint16_t)((idx[0] | (idx[1] << 4)) | ((idx[2] | (idx[3] << 4)) << 8));
         *reinterpret_cast<uint16_t *>(packed + r * (K / 2) + (int64_t)b * (kRot / 2) + 2 * lane) = two;
     }
