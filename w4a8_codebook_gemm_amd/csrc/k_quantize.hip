@@ -26,7 +26,7 @@
 //     thresholds (c_j + c_{j+1}) / 2, cell bounds by binary search over the sorted values,
 //     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
 //     codebook = (float)c.
-//  6. k_assign_pack: per row, rotate and normalise again (the arithmetic of steps 1 and 2),
+//  6. k_assign_pack: per block, rotate and normalise again (the arithmetic of steps 1 and 2),
 //     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 } (decided by an
 //     equivalent fp32 compare), two indices per byte, even element in the low nibble.
 #include <atomic>
@@ -574,14 +574,18 @@ __global__ __launch_bounds__(kLloydThreads) void k_lloyd(const uint32_t *__restr
     if (j < kLevels) cb[j] = (float)c[j];
 }
 
-// Per row: rotate and normalise every 256-block again (lane l holds elements 4l .. 4l+3, in
-// group l / 4), take each value's nearest level and pack two indices per byte.
+// Per 256-block on one 16-lane DPP row (four blocks per wave, 16 per workgroup): rotate it
+// again with the row transform (bit-identical to the lane transform of steps 1 and 2 up to
+// the sign of a zero, which no output depends on), so that each lane holds one whole group of
+// 16 values; normalise, take each value's nearest level and store the lane's 16 indices as 8
+// bytes, two per byte.
+constexpr int kAssignThreads = 256;
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict__ w, int64_t K,
-                                                          const float *__restrict__ s_ch,
-                                                          const uint8_t *__restrict__ s_rel,
-                                                          const float *__restrict__ cb,
-                                                          int8_t *__restrict__ packed) {
+__global__ __launch_bounds__(kAssignThreads) void k_assign_pack(const void *__restrict__ w, int64_t N, int64_t K,
+                                                                const float *__restrict__ s_ch,
+                                                                const uint8_t *__restrict__ s_rel,
+                                                                const float *__restrict__ cb,
+                                                                int8_t *__restrict__ packed) {
     // each midpoint (cb[j] + cb[j+1]) / 2, exact in fp64, as the largest fp32 at or below it:
     // for an fp32 v, (double)v > mid exactly when v > that fp32, so one fp32 compare per
     // level decides what the fp64 compare decides
@@ -593,25 +597,29 @@ __global__ __launch_bounds__(kThreads) void k_assign_pack(const void *__restrict
         thr[threadIdx.x] = f;
     }
     __syncthreads();
-    const int64_t r = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nblk = (int)(K / kRot);
-    const float rmax = s_ch[r];
-    for (int b = wave; b < nblk; b += kWaves) {
-        float v[4];
-        load4<BF16>(w, r * K + (int64_t)b * kRot + 4 * lane, v);
-        fwht256_lane4(v, lane);
-        normalise4(v, rmax, s_rel[r * (K / kGroup) + b * 16 + (lane >> 2)]);
-        // the number of thresholds below v, by a four-step binary search over the ascending
+    const int t16 = threadIdx.x & 15, h = fwht_row16_nibble(t16);
+    const int64_t nblk = K / kRot;
+    const int64_t gb = (int64_t)blockIdx.x * (kAssignThreads / 16) + (threadIdx.x >> 4);
+    const bool live = gb < N * nblk;   // the same for the 16 lanes of a row
+    const int64_t g0 = live ? gb : 0;
+    const int64_t r = g0 / nblk, b = g0 - r * nblk;
+    float v[16];
+    load16<BF16>(w, r * K + b * kRot + 16 * h, v);
+    fwht256_row16(v, t16);
+    const float d = s_ch[r] * e4m3_to_f32(s_rel[r * (K / kGroup) + b * 16 + h]);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+        const float x = (d > 0.0f) ? v[q] / d : 0.0f;
+        // the number of thresholds below x, by a four-step binary search over the ascending
         // thresholds (the same count as comparing with all fifteen)
-        int idx[4] = {0, 0, 0, 0};
+        int idx = 0;
 #pragma unroll
-        for (int step = 8; step >= 1; step >>= 1)
-#pragma unroll
-            for (int q = 0; q < 4; q++) idx[q] += (v[q] > thr[idx[q] + step - 1]) ? step : 0;
-        const uint16_t two = (uint16_t)((idx[0] | (idx[1] << 4)) | ((idx[2] | (idx[3] << 4)) << 8));
-        *reinterpret_cast<uint16_t *>(packed + r * (K / 2) + (int64_t)b * (kRot / 2) + 2 * lane) = two;
+        for (int step = 8; step >= 1; step >>= 1) idx += (x > thr[idx + step - 1]) ? step : 0;
+        if (q < 8) lo |= (uint32_t)idx << (4 * q);
+        else hi |= (uint32_t)idx << (4 * (q - 8));
     }
+    if (live) *reinterpret_cast<uint2 *>(packed + r * (K / 2) + b * (kRot / 2) + 8 * h) = make_uint2(lo, hi);
 }
 
 // Scratch of the no-allocation entry point: one array per device, as large as the largest
@@ -739,12 +747,13 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_lloyd, dim3(1), dim3(kLloydThreads), 0, stream, keys, P, L.S, cb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned ablocks = (unsigned)((NK / kRot + kAssignThreads / 16 - 1) / (kAssignThreads / 16));
     if (w_bf16)
-        hipLaunchKernelGGL(k_assign_pack<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_ch, s_rel, cb,
-                           packed);
+        hipLaunchKernelGGL(k_assign_pack<true>, dim3(ablocks), dim3(kAssignThreads), 0, stream, w, N, K, s_ch, s_rel,
+                           cb, packed);
     else
-        hipLaunchKernelGGL(k_assign_pack<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_ch, s_rel, cb,
-                           packed);
+        hipLaunchKernelGGL(k_assign_pack<false>, dim3(ablocks), dim3(kAssignThreads), 0, stream, w, N, K, s_ch, s_rel,
+                           cb, packed);
     return hipGetLastError();
 }
 
