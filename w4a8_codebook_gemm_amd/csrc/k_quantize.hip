@@ -205,6 +205,52 @@ __global__ __launch_bounds__(64 * kSampleWaves) void k_sample_keys(
     for (int64_t i = S + t; i < P2; i += nthreads) keys[i] = 0xFFFFFFFFu;
 }
 
+// Step 1 on 16-lane DPP rows for rows of up to 2 x 64 blocks: lane row g rotates blocks g and
+// g + (lane rows) with the row transform (bit-identical to the lane transform up to the sign
+// of a zero, which neither maximum sees), so that each lane holds one whole group of 16: its
+// group maximum needs no exchange.  The row maximum goes through the waves' maxima in LDS.
+template <bool BF16, int R>
+__global__ __launch_bounds__(1024) void k_rotate_scale16(const void *__restrict__ w, int64_t K,
+                                                         uint8_t *__restrict__ s_rel, float *__restrict__ s_ch) {
+    __shared__ float red[16];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    const int rows16 = blockDim.x >> 4, g = tid >> 4, t16 = tid & 15, h = fwht_row16_nibble(t16);
+    const int nblk = (int)(K / kRot);
+    float v[R][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const int b = g + q * rows16;
+        // an absent block re-reads the last one (all 16 lanes of its row alike) and is ignored
+        load16<BF16>(w, r * K + (int64_t)(b < nblk ? b : nblk - 1) * kRot + 16 * h, v[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        fwht256_row16(v[q], t16);
+        if (g + q * rows16 < nblk)
+#pragma unroll
+            for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(v[q][i]));
+    }
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) amax = fmaxf(amax, __shfl_xor(amax, sh));
+    if ((tid & 63) == 0) red[wave] = amax;
+    __syncthreads();
+    float rmax = red[0];
+    for (int i = 1; i < nwaves; i++) rmax = fmaxf(rmax, red[i]);
+    if (tid == 0) s_ch[r] = rmax;
+#pragma unroll
+    for (int q = 0; q < R; q++) {
+        const int b = g + q * rows16;
+        if (b < nblk) {
+            float gm = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i++) gm = fmaxf(gm, fabsf(v[q][i]));
+            s_rel[r * (K / kGroup) + b * 16 + h] = (uint8_t)((rmax > 0.0f) ? f32_to_e4m3_rne(gm / rmax) : 0u);
+        }
+    }
+}
+
 // Sampled fits (N*K > 2^20) by block: k_sample_keys rotates a whole 256-block for every
 // sample, about three times per block at the MLP shapes.  These kernels rotate each block
 // that holds samples once instead.  For a chunk of kChunkBlocks 256-blocks at a time they
@@ -663,10 +709,27 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
     const int64_t NK = N * K;
     hipError_t e;
 
-    if (w_bf16)
+    const int64_t nblk = K / kRot;
+    if (nblk <= 128) {
+        // 16 lanes per block, whole waves, one or two rounds
+        const int rounds = nblk <= 64 ? 1 : 2;
+        const unsigned threads = (unsigned)(((nblk + rounds - 1) / rounds * 16 + 63) / 64 * 64);
+        if (rounds == 1) {
+            if (w_bf16)
+                hipLaunchKernelGGL((k_rotate_scale16<true, 1>), dim3((unsigned)N), dim3(threads), 0, stream, w, K, s_rel, s_ch);
+            else
+                hipLaunchKernelGGL((k_rotate_scale16<false, 1>), dim3((unsigned)N), dim3(threads), 0, stream, w, K, s_rel, s_ch);
+        } else {
+            if (w_bf16)
+                hipLaunchKernelGGL((k_rotate_scale16<true, 2>), dim3((unsigned)N), dim3(threads), 0, stream, w, K, s_rel, s_ch);
+            else
+                hipLaunchKernelGGL((k_rotate_scale16<false, 2>), dim3((unsigned)N), dim3(threads), 0, stream, w, K, s_rel, s_ch);
+        }
+    } else if (w_bf16) {
         hipLaunchKernelGGL(k_rotate_scale<true>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_rel, s_ch);
-    else
+    } else {
         hipLaunchKernelGGL(k_rotate_scale<false>, dim3((unsigned)N), dim3(kThreads), 0, stream, w, K, s_rel, s_ch);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     if (NK > kSampleMax) {
