@@ -6,27 +6,31 @@
 // before quantisation, group 256) and "Reproducing" (the seed pins the codebook fit, which
 // samples); "Qwen3.8-27B-W4A8 (for ComfyUI)", section "Model Overview".
 //
-// Steps, each a kernel on the caller's stream:
-//  1. k_rotate_scale: per row, rotate every 256-block (the same lane-level transform as
-//     the activation kernel), s_channel = max |w_rot|, s_rel = E4M3FN(group max / s_channel)
-//     rounded to nearest even.
-//  2. k_sample_keys: S = min(N*K, 2^20) fit values v = w_rot / (s_channel * dec(s_rel)) --
-//     all of them, or those at positions floor(u_i * N*K / 2^64) with u_i the i-th
-//     SplitMix64 output for `seed` -- as uint32 keys whose unsigned order is the fp32 total
-//     order (-0 before +0); padded with 0xFFFFFFFF to a power of two.  Each wave rotates the
-//     256-block that holds its value (or, with every value taken, a whole block) with the
-//     arithmetic of step 1, so the normalised values are never stored: the workspace holds
-//     only the sample and its prefix sums, at most 12 MiB whatever N and K.
-//  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans).
+// Steps, each a kernel (or a few) on the caller's stream:
+//  1. k_rotate_scale16 (k_rotate_scale for rows over 128 blocks): per row, rotate every
+//     256-block, s_channel = max |w_rot|, s_rel = E4M3FN(group max / s_channel) rounded to
+//     nearest even.  The row transform runs each block on a 16-lane DPP row; it matches the
+//     lane transform bit for bit except for the sign of an exact zero, which maxima of |v|
+//     do not see.
+//  2. Sampling: S = min(N*K, 2^20) fit values v = w_rot / (s_channel * dec(s_rel)) -- all of
+//     them (k_sample_keys), or those at positions floor(u_i * N*K / 2^64) with u_i the i-th
+//     SplitMix64 output for `seed` (k_sample_count / _scan_* / _list / _blocks: the samples
+//     bucketed by block, each block rotated once) -- as uint32 keys whose unsigned order is
+//     the fp32 total order (-0 before +0); padded with 0xFFFFFFFF to a power of two.  The
+//     values come from the lane transform (the sign of a zero can reach a codebook level),
+//     and are never stored beyond the sample: the workspace holds only the sample and its
+//     prefix sums, at most 12 MiB whatever N and K.
+//  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans, up to three of
+//     the longer passes per sweep).
 //  4. k_prefix_*: running fp64 sums of the sorted values in the blocked order (blocks of
 //     kPrefixBlock values summed left to right from 0, the block offsets left to right over
 //     the block totals, then offset + block-local sum; the order fixes the rounding, which
 //     the codebook bits depend on).  One lane per block, so 1024 blocks run at once.
 //  5. k_lloyd: one workgroup runs Lloyd's iteration in fp64 from the mid-quantile start:
-//     thresholds (c_j + c_{j+1}) / 2, cell bounds by binary search over the sorted values,
-//     cell means from the prefix sums, at most 100 updates, stop when no bound moves;
+//     thresholds (c_j + c_{j+1}) / 2, cell bounds by search over the sorted values, cell
+//     means from the prefix sums, at most 100 updates, stop when no bound moves;
 //     codebook = (float)c.
-//  6. k_assign_pack: per block, rotate and normalise again (the arithmetic of steps 1 and 2),
+//  6. k_assign_pack: per block (row transform, as in step 1), normalise again,
 //     idx = #{ j < 15 : (double)v > ((double)cb[j] + (double)cb[j+1]) / 2 } (decided by an
 //     equivalent fp32 compare), two indices per byte, even element in the low nibble.
 #include <atomic>
