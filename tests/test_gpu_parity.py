@@ -137,11 +137,26 @@ def check_quant(w, W, seed, dtype=torch.float32):
     return L, q
 
 
-@pytest.mark.parametrize("N,K,seed", [(256, 512, 0), (1, 256, 3), (2048, 1024, 42), (300, 768, 7)])
+# rows of 1 to 128 blocks take the row-transform scale kernel (one or two rounds), longer
+# rows the lane-transform one; 40 x 33024 also samples (over 2^20 values)
+@pytest.mark.parametrize("N,K,seed", [(256, 512, 0), (1, 256, 3), (2048, 1024, 42), (300, 768, 7),
+                                      (64, 32768, 11), (40, 33024, 5)])
 def test_quantize_bit_exact(w, N, K, seed):
     say(f"quantize N={N} K={K} seed={seed}")
     W = S.weights(N, K, seed=seed)
     check_quant(w, W, seed)
+
+
+def test_quantize_zero_rows_and_blocks(w):
+    # exact zeros of both signs: a zero row, a -0 row, a zero block and a -0 block (the row
+    # transform may give -0 where the lane transform gives +0; no output may show it)
+    say("quantize zero rows and blocks")
+    W = S.weights(64, 1024, seed=13)
+    W[3] = 0.0
+    W[5] = -0.0
+    W[7, 256:512] = 0.0
+    W[9, 512:768] = -0.0
+    check_quant(w, W, 13)
 
 
 def test_quantize_bf16_input(w):
