@@ -334,37 +334,59 @@ __global__ __launch_bounds__(kCountThreads) void k_sample_list(uint64_t seed, in
     if (blk >= c0 && blk < c1) list[atomicAdd(&cur[blk - c0], 1u)] = (uint32_t)i;
 }
 
-// One wave per block of the chunk: rotate and normalise it as k_sample_keys does, then
-// write the key of each sample it holds.  The block's loads go out before its sample count
-// is known; lane t takes the block's t-th listed sample and fetches its value from the lane
-// that holds it (up to 64 samples at a time).
+// Four blocks of the chunk per wave: rotate and normalise each as k_sample_keys does, then
+// write the key of each sample it holds.  Every block's loads and sample counts go out
+// first, then the first 64 listed samples of every block (lane t takes the t-th), so a wave
+// waits for memory twice for its four blocks; each sample's value comes from the lane that
+// holds it.
+constexpr int kSampleNB = 4;
 template <bool BF16>
 __global__ __launch_bounds__(64 * kSampleWaves) void k_sample_blocks(
     const void *__restrict__ w, int64_t K, int64_t NK, uint64_t seed, int64_t c0, int64_t c1,
     const float *__restrict__ s_ch, const uint8_t *__restrict__ s_rel, const uint32_t *__restrict__ cnt,
     const uint32_t *__restrict__ list, uint32_t *__restrict__ keys) {
     const int lane = threadIdx.x & 63;
-    const int64_t blk = c0 + (int64_t)blockIdx.x * kSampleWaves + (threadIdx.x >> 6);
-    if (blk >= c1) return;
-    const int64_t pos0 = blk * kRot, r = pos0 / K, blk0 = pos0 - r * K;
-    float v[4];
-    load4<BF16>(w, pos0 + 4 * lane, v);
-    const uint32_t code = s_rel[r * (K / kGroup) + blk0 / kGroup + (lane >> 2)];
-    const float rmax = s_ch[r];
-    const uint32_t q0 = cnt[blk - c0], q1 = cnt[blk - c0 + 1];
-    if (q0 == q1) return;
-    fwht256_lane4(v, lane);
-    normalise4(v, rmax, code);
-    for (uint32_t qb = q0; qb < q1; qb += 64) {
-        const uint32_t q = qb + (uint32_t)lane;
-        const bool mine = q < q1;
-        const int64_t i = mine ? (int64_t)list[q] : 0;
-        const int e = mine ? (int)(sample_pos(seed, i, NK) - pos0) : 0;   // the sample's element
-        const int src = e >> 2;
-        const float a0 = __shfl(v[0], src), a1 = __shfl(v[1], src), a2 = __shfl(v[2], src), a3 = __shfl(v[3], src);
-        const int c = e & 3;
-        const float val = c == 0 ? a0 : c == 1 ? a1 : c == 2 ? a2 : a3;
-        if (mine) keys[i] = f32_to_key(val);
+    const int64_t first = c0 + ((int64_t)blockIdx.x * kSampleWaves + (threadIdx.x >> 6)) * kSampleNB;
+    if (first >= c1) return;
+    float v[kSampleNB][4], rmax[kSampleNB];
+    uint32_t code[kSampleNB], q0[kSampleNB], q1[kSampleNB];
+    int64_t pos0[kSampleNB];
+#pragma unroll
+    for (int b = 0; b < kSampleNB; b++) {
+        const int64_t blk = first + b < c1 ? first + b : first;   // past the chunk: a copy of the first, no samples
+        pos0[b] = blk * kRot;
+        const int64_t r = pos0[b] / K, blk0 = pos0[b] - r * K;
+        load4<BF16>(w, pos0[b] + 4 * lane, v[b]);
+        code[b] = s_rel[r * (K / kGroup) + blk0 / kGroup + (lane >> 2)];
+        rmax[b] = s_ch[r];
+        q0[b] = cnt[blk - c0];
+        q1[b] = first + b < c1 ? cnt[blk - c0 + 1] : q0[b];
+    }
+    uint32_t li[kSampleNB];
+#pragma unroll
+    for (int b = 0; b < kSampleNB; b++) {
+        const uint32_t q = q0[b] + (uint32_t)lane;
+        li[b] = list[q < q1[b] ? q : 0u];   // entry 0 is in the list's storage whatever the count
+    }
+#pragma unroll
+    for (int b = 0; b < kSampleNB; b++) {
+        fwht256_lane4(v[b], lane);
+        normalise4(v[b], rmax[b], code[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < kSampleNB; b++) {
+        for (uint32_t qb = q0[b]; qb < q1[b]; qb += 64) {
+            const uint32_t q = qb + (uint32_t)lane;
+            const bool mine = q < q1[b];
+            const int64_t i = !mine ? 0 : (qb == q0[b] ? (int64_t)li[b] : (int64_t)list[q]);
+            const int e = mine ? (int)(sample_pos(seed, i, NK) - pos0[b]) : 0;   // the sample's element
+            const int src = e >> 2;
+            const float a0 = __shfl(v[b][0], src), a1 = __shfl(v[b][1], src), a2 = __shfl(v[b][2], src),
+                        a3 = __shfl(v[b][3], src);
+            const int c = e & 3;
+            const float val = c == 0 ? a0 : c == 1 ? a1 : c == 2 ? a2 : a3;
+            if (mine) keys[i] = f32_to_key(val);
+        }
     }
 }
 
@@ -762,7 +784,7 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
             hipLaunchKernelGGL(k_sample_list, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cur,
                                list);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            const unsigned bgrid = (unsigned)((c1 - c0 + kSampleWaves - 1) / kSampleWaves);
+            const unsigned bgrid = (unsigned)((c1 - c0 + kSampleWaves * kSampleNB - 1) / (kSampleWaves * kSampleNB));
             if (w_bf16)
                 hipLaunchKernelGGL(k_sample_blocks<true>, dim3(bgrid), dim3(64 * kSampleWaves), 0, stream, w, K, NK,
                                    seed, c0, c1, s_ch, s_rel, cnt, list, keys);
