@@ -258,12 +258,12 @@ __global__ __launch_bounds__(1024) void k_rotate_scale16(const void *__restrict_
 // Sampled fits (N*K > 2^20) by block: k_sample_keys rotates a whole 256-block for every
 // sample, about three times per block at the MLP shapes.  These kernels rotate each block
 // that holds samples once instead.  For a chunk of kChunkBlocks 256-blocks at a time they
-// count the samples per block, turn the counts into offsets, list each block's sample
-// indices (in any order) and let one wave per block rotate it and write keys[i] for each
-// of its samples i -- the same keys at the same places as k_sample_keys writes.  The counts,
-// cursors and list live in the prefix-sum area of the workspace, unused until the sort is
-// done.
-constexpr int64_t kChunkBlocks = (1 << 19) - 1024;   // with the scratch below, fills the prefix area
+// count the samples per block (each sample parking its rank within its block), turn the
+// counts into offsets, list each block's sample indices at offset + rank (any order within
+// a block) and let a wave rotate each block and write keys[i] for each of its samples i --
+// the same keys at the same places as k_sample_keys writes.  The counts and the list live
+// in the prefix-sum area of the workspace, unused until the sort is done.
+constexpr int64_t kChunkBlocks = (1 << 19) - 1024;   // blocks per pass; the scratch below fits the prefix area
 constexpr int kCountThreads = 256;
 
 __device__ __forceinline__ int64_t sample_pos(uint64_t seed, int64_t i, int64_t NK) {
@@ -276,17 +276,20 @@ __global__ __launch_bounds__(kCountThreads) void k_fill_u32(uint32_t *__restrict
     for (int64_t i = t; i < n; i += stride) p[i] = v;
 }
 
+// Counts the samples per block; each sample of the chunk parks its rank within its block
+// in keys[i] (that key is written only later, by k_sample_blocks).
 __global__ __launch_bounds__(kCountThreads) void k_sample_count(uint64_t seed, int64_t S, int64_t NK, int64_t c0,
-                                                                int64_t c1, uint32_t *__restrict__ cnt) {
+                                                                int64_t c1, uint32_t *__restrict__ cnt,
+                                                                uint32_t *__restrict__ keys) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= S) return;
     const int64_t blk = sample_pos(seed, i, NK) / kRot;
-    if (blk >= c0 && blk < c1) atomicAdd(&cnt[blk - c0], 1u);
+    if (blk >= c0 && blk < c1) keys[i] = atomicAdd(&cnt[blk - c0], 1u);
 }
 
-// cnt[0 .. n) -> exclusive offsets (integers: exact in any order), cnt[n] = total; cur = a
-// copy of the offsets.  Segments of 1024 counts: each workgroup scans its own in LDS and
-// records the segment's total; then each adds the totals of the segments before it.
+// cnt[0 .. n) -> exclusive offsets (integers: exact in any order), cnt[n] = total.  Segments
+// of 1024 counts: each workgroup scans its own in LDS and records the segment's total; then
+// each adds the totals of the segments before it.
 constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void k_sample_scan_seg(uint32_t *__restrict__ cnt, int64_t n,
                                                                   uint32_t *__restrict__ segsum) {
@@ -306,8 +309,8 @@ __global__ __launch_bounds__(kScanThreads) void k_sample_scan_seg(uint32_t *__re
     if (t == kScanThreads - 1) segsum[blockIdx.x] = sh[t];
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_sample_scan_add(uint32_t *__restrict__ cnt, uint32_t *__restrict__ cur,
-                                                                  int64_t n, const uint32_t *__restrict__ segsum) {
+__global__ __launch_bounds__(kScanThreads) void k_sample_scan_add(uint32_t *__restrict__ cnt, int64_t n,
+                                                                  const uint32_t *__restrict__ segsum) {
     __shared__ uint32_t base;
     const int t = threadIdx.x;
     const int seg = blockIdx.x;
@@ -317,21 +320,19 @@ __global__ __launch_bounds__(kScanThreads) void k_sample_scan_add(uint32_t *__re
     __syncthreads();
     const uint32_t b = base;
     const int64_t i = (int64_t)seg * kScanThreads + t;
-    if (i < n) {
-        const uint32_t c = cnt[i] + b;
-        cnt[i] = c;
-        cur[i] = c;
-    }
+    if (i < n) cnt[i] += b;
     if (seg == (int)gridDim.x - 1 && t == 0) cnt[n] = b + segsum[seg];
 }
 
+// Lists each block's samples at its offset plus the rank k_sample_count parked.
 __global__ __launch_bounds__(kCountThreads) void k_sample_list(uint64_t seed, int64_t S, int64_t NK, int64_t c0,
-                                                               int64_t c1, uint32_t *__restrict__ cur,
+                                                               int64_t c1, const uint32_t *__restrict__ off,
+                                                               const uint32_t *__restrict__ keys,
                                                                uint32_t *__restrict__ list) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= S) return;
     const int64_t blk = sample_pos(seed, i, NK) / kRot;
-    if (blk >= c0 && blk < c1) list[atomicAdd(&cur[blk - c0], 1u)] = (uint32_t)i;
+    if (blk >= c0 && blk < c1) list[off[blk - c0] + keys[i]] = (uint32_t)i;
 }
 
 // Four blocks of the chunk per wave: rotate and normalise each as k_sample_keys does, then
@@ -759,14 +760,13 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     if (NK > kSampleMax) {
-        // S = 2^20 = P2: no padding.  Counts, cursors and the list in the prefix-sum area.
-        static_assert(round256((kChunkBlocks + 1) * 4) + kChunkBlocks * 4 + kSampleMax * 4 +
+        // S = 2^20 = P2: no padding.  Counts and the list in the prefix-sum area.
+        static_assert(round256((kChunkBlocks + 1) * 4) + kSampleMax * 4 +
                               4 * ((kChunkBlocks + kScanThreads - 1) / kScanThreads) <=
                           round256((kSampleMax + 1) * 8),
                       "sampling scratch inside the prefix area");
         uint32_t *cnt = reinterpret_cast<uint32_t *>(P);
-        uint32_t *cur = cnt + round256((kChunkBlocks + 1) * 4) / 4;
-        uint32_t *list = cur + kChunkBlocks;
+        uint32_t *list = cnt + round256((kChunkBlocks + 1) * 4) / 4;
         uint32_t *segsum = list + kSampleMax;
         const int64_t nb = NK / kRot;
         const unsigned cgrid = (unsigned)((L.S + kCountThreads - 1) / kCountThreads);
@@ -774,15 +774,16 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
             const int64_t c1 = c0 + kChunkBlocks < nb ? c0 + kChunkBlocks : nb;
             hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(kCountThreads), 0, stream, cnt, c1 - c0 + 1, 0u);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_sample_count, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cnt);
+            hipLaunchKernelGGL(k_sample_count, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cnt,
+                               keys);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             const unsigned nseg = (unsigned)((c1 - c0 + kScanThreads - 1) / kScanThreads);
             hipLaunchKernelGGL(k_sample_scan_seg, dim3(nseg), dim3(kScanThreads), 0, stream, cnt, c1 - c0, segsum);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_sample_scan_add, dim3(nseg), dim3(kScanThreads), 0, stream, cnt, cur, c1 - c0, segsum);
+            hipLaunchKernelGGL(k_sample_scan_add, dim3(nseg), dim3(kScanThreads), 0, stream, cnt, c1 - c0, segsum);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            hipLaunchKernelGGL(k_sample_list, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cur,
-                               list);
+            hipLaunchKernelGGL(k_sample_list, dim3(cgrid), dim3(kCountThreads), 0, stream, seed, L.S, NK, c0, c1, cnt,
+                               keys, list);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             const unsigned bgrid = (unsigned)((c1 - c0 + kSampleWaves * kSampleNB - 1) / (kSampleWaves * kSampleNB));
             if (w_bf16)
