@@ -478,6 +478,65 @@ __global__ __launch_bounds__(kSortTile / 2) void k_bitonic_tile(uint32_t *keys, 
     keys[base + t + kSortTile / 2] = s[t + kSortTile / 2];
 }
 
+// LSD radix sort of a full 2^20-key sample (S = P2): four stable passes of 8-bit digits,
+// ping-ponging between the keys and a copy in the prefix-sum area (idle until the sort is
+// done).  Per pass: each 1024-key tile counts its digits (k_radix_hist, digit-major
+// counts), the counts are scanned into offsets (k_sample_scan_*), and each tile writes its
+// keys to offset + rank, the rank counting the equal digits before the key in the tile:
+// wave ballots over the digit's bits find the equal lanes, per-wave counts in LDS order the
+// waves and rounds.  The sorted keys are the bitonic network's, key for key.
+constexpr int kRadixTile = 1024;
+constexpr int kRadixThreads = 256;
+
+__global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const uint32_t *__restrict__ in, int shift, int ntiles,
+                                                              uint32_t *__restrict__ hist) {
+    __shared__ uint32_t h[256];
+    const int t = threadIdx.x;
+    h[t] = 0u;
+    __syncthreads();
+    const uint32_t *tile = in + (int64_t)blockIdx.x * kRadixTile;
+#pragma unroll
+    for (int q = 0; q < kRadixTile / kRadixThreads; q++) atomicAdd(&h[(tile[q * kRadixThreads + t] >> shift) & 255u], 1u);
+    __syncthreads();
+    hist[(int64_t)t * ntiles + blockIdx.x] = h[t];
+}
+
+__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(const uint32_t *__restrict__ in,
+                                                                 uint32_t *__restrict__ out, int shift, int ntiles,
+                                                                 const uint32_t *__restrict__ off) {
+    __shared__ uint32_t run[256];                        // keys of each digit in earlier rounds
+    __shared__ uint32_t wcnt[kRadixThreads / 64][256];   // this round's count per wave and digit
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    run[t] = 0u;
+    const uint32_t *tile = in + (int64_t)blockIdx.x * kRadixTile;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int round = 0; round < kRadixTile / kRadixThreads; round++) {
+#pragma unroll
+        for (int w = 0; w < kRadixThreads / 64; w++) wcnt[w][t] = 0u;
+        const uint32_t key = tile[round * kRadixThreads + t];
+        const uint32_t d = (key >> shift) & 255u;
+        unsigned long long peers = ~0ull;
+#pragma unroll
+        for (int bit = 0; bit < 8; bit++) {
+            const unsigned long long m = __ballot((d >> bit) & 1u);
+            peers &= ((d >> bit) & 1u) ? m : ~m;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & below);
+        __syncthreads();   // the counts are zeroed
+        if (rank == 0) wcnt[wave][d] = (uint32_t)__popcll(peers);   // the lowest lane of its digit
+        __syncthreads();
+        uint32_t pre = run[d];
+        for (int w = 0; w < wave; w++) pre += wcnt[w][d];
+        out[off[(int64_t)d * ntiles + blockIdx.x] + pre + rank] = key;
+        __syncthreads();   // every lane has read run and wcnt
+        uint32_t add = 0u;
+#pragma unroll
+        for (int w = 0; w < kRadixThreads / 64; w++) add += wcnt[w][t];
+        run[t] += add;
+        __syncthreads();
+    }
+}
+
 // Running fp64 sums P[0] = 0, P[i+1] = P[i] + value(i), strictly in index order.
 constexpr int kPrefixBlock = 1024;
 constexpr int kPrefixThreads = (int)(kSampleMax / kPrefixBlock);  // one lane per block
@@ -806,6 +865,33 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
+    if (L.S == kSampleMax) {
+        // radix passes: keys -> copy -> keys -> copy -> keys, in the prefix-sum area the copy,
+        // the digit counts (+ their total) and the scan's segment totals
+        const int ntiles = (int)(kSampleMax / kRadixTile);
+        const int64_t ncnt = (int64_t)256 * ntiles;
+        static_assert(kSampleMax * 4 + round256(((size_t)256 * (kSampleMax / kRadixTile) + 1) * 4) +
+                              4 * ((256 * (kSampleMax / kRadixTile) + kScanThreads - 1) / kScanThreads) <=
+                          round256((kSampleMax + 1) * 8),
+                      "radix scratch inside the prefix area");
+        uint32_t *copy = reinterpret_cast<uint32_t *>(P);
+        uint32_t *hist = copy + kSampleMax;
+        uint32_t *segsum = hist + round256((size_t)(ncnt + 1) * 4) / 4;
+        const unsigned nseg = (unsigned)((ncnt + kScanThreads - 1) / kScanThreads);
+        for (int pass = 0; pass < 4; pass++) {
+            const uint32_t *in = (pass & 1) ? copy : keys;
+            uint32_t *out = (pass & 1) ? keys : copy;
+            hipLaunchKernelGGL(k_radix_hist, dim3(ntiles), dim3(kRadixThreads), 0, stream, in, 8 * pass, ntiles, hist);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_sample_scan_seg, dim3(nseg), dim3(kScanThreads), 0, stream, hist, ncnt, segsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_sample_scan_add, dim3(nseg), dim3(kScanThreads), 0, stream, hist, ncnt, segsum);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(k_radix_scatter, dim3(ntiles), dim3(kRadixThreads), 0, stream, in, out, 8 * pass, ntiles,
+                               hist);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    } else {
     const unsigned tiles = (unsigned)(L.P2 / kSortTile);
     hipLaunchKernelGGL(k_bitonic_tile, dim3(tiles), dim3(kSortTile / 2), 0, stream, keys, (int64_t)2,
                        (int64_t)kSortTile);
@@ -826,6 +912,7 @@ hipError_t launch_quantize(const void *w, int w_bf16, int64_t N, int64_t K, uint
         }
         hipLaunchKernelGGL(k_bitonic_tile, dim3(tiles), dim3(kSortTile / 2), 0, stream, keys, k, k);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     }
 
     const unsigned pblocks = (unsigned)((L.S + (int64_t)kPrefixBlock * kPrefixWave - 1) / ((int64_t)kPrefixBlock * kPrefixWave));
