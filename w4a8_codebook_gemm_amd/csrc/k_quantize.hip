@@ -20,8 +20,9 @@
 //     values come from the lane transform (the sign of a zero can reach a codebook level),
 //     and are never stored beyond the sample: the workspace holds only the sample and its
 //     prefix sums, at most 12 MiB whatever N and K.
-//  3. bitonic sort of the keys (LDS tiles of 2048 keys for the short spans, up to three of
-//     the longer passes per sweep).
+//  3. sort of the keys: a full 2^20-key sample by an LSD radix sort (four stable passes of
+//     8-bit digits), smaller ones by a bitonic network (LDS tiles of 2048 keys for the short
+//     spans, up to three of the longer passes per sweep).
 //  4. k_prefix_*: running fp64 sums of the sorted values in the blocked order (blocks of
 //     kPrefixBlock values summed left to right from 0, the block offsets left to right over
 //     the block totals, then offset + block-local sum; the order fixes the rounding, which
