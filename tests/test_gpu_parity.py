@@ -70,9 +70,11 @@ def sample(n, count, seed):
 # ----------------------------------------------------------------------------- prepare
 
 # K from one block (one 64-thread workgroup) through two register rounds (K <= 32768) to the
-# two-pass path for longer rows
+# two-pass path for longer rows; the two fp32 prefill launches the benchmark times (2048 tokens
+# of the MLP input and of the hidden activation) are included as they are timed
 PREP_CASES = [(4, 512, "f32"), (4, 512, "bf16"), (1, 256, "f32"), (3, 5120, "f32"),
               (2, 17408, "bf16"), (37, 768, "f32"), (5, 20736, "f32"), (2048, 5120, "bf16"),
+              (2048, 5120, "f32"), (2048, 17408, "f32"),
               (3, 32768, "f32"), (3, 33024, "bf16"), (2, 65536, "f32")]
 
 
