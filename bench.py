@@ -165,8 +165,9 @@ def read_ceiling(torch, nbytes, copies=COPIES):
     16-byte loads, each workgroup on a contiguous share) over `copies` distinct buffers, as
     the decode kernels rotate through weight copies, timed like the kernels.  The best over
     workgroup widths 256 / 512 / 1024 threads, 2 / 4 / 8 loads in flight per thread and one or
-    two workgroups per compute unit.  Returns (GB/s, config) or None when the helper is not
-    built."""
+    two workgroups per compute unit.  Returns (GB/s, config, GB/s of the decode GEMV's own
+    launch shape: one 1024-thread workgroup per CU, two loads in flight per lane) or None when
+    the helper is not built."""
     lib = probes()
     if lib is None:
         return None
@@ -174,7 +175,7 @@ def read_ceiling(torch, nbytes, copies=COPIES):
     n = nbytes // 16 * 16
     bufs = [torch.full((n,), c + 1, dtype=torch.uint8, device="cuda") for c in range(copies)]
     sink = torch.zeros(2 * cus * 1024, dtype=torch.int32, device="cuda")
-    best, cfg = 0.0, None
+    best, cfg, own = 0.0, None, None
     for per_cu in (1, 2):
         for threads in (256, 512, 1024):
             for depth in (2, 4, 8):
@@ -188,6 +189,8 @@ def read_ceiling(torch, nbytes, copies=COPIES):
                             raise RuntimeError(f"bench_read_launch: HIP error {rc}")
                 g = make_graph(torch, launch)
                 t = time_kernel_graph(torch, g) / copies
+                if (per_cu, threads, depth) == (1, 1024, 2):
+                    own = n / t / 1e9
                 if n / t / 1e9 > best:
                     best, cfg = n / t / 1e9, dict(workgroups_per_cu=per_cu, threads=threads,
                                                   loads_in_flight_per_thread=depth,
@@ -196,7 +199,7 @@ def read_ceiling(torch, nbytes, copies=COPIES):
                 del g
     del bufs
     torch.cuda.empty_cache()
-    return best, cfg
+    return best, cfg, own
 
 
 def stream_ceiling(torch, in_bytes, copies=COPIES):
@@ -394,10 +397,13 @@ def decode(w, torch, S, args, shapes):
                     avg_launch_us_sustained=round(t_gu_sustained * 1e6, 3))
     rcc = read_ceiling(torch, int(per_gu))
     if rcc:
-        rc, cfg = rcc
+        rc, cfg, own = rcc
         roofline["read_ceiling_gbs"] = round(rc, 1)
         roofline["read_ceiling_config"] = cfg
         roofline["frac_of_read_ceiling"] = round(ach / rc, 4)
+        # the same plain read in the kernel's own launch shape: what its fixed costs are measured against
+        roofline["read_same_shape_gbs"] = round(own, 1)
+        roofline["frac_of_read_same_shape"] = round(ach / own, 4)
         log(f"plain read of {per_gu / 1e6:.1f} MB per launch: {rc:.1f} GB/s ({cfg}); the fused gate+up "
             f"launch reaches {ach / rc * 100:.1f}% of it")
     down_k = dict(kernel="k_gemv<1,1,1> (fused rotate + quantise + W4A8 GEMV of down, fp32 x)",
