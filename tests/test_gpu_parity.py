@@ -735,6 +735,41 @@ def test_bench_down_launch_full_size(w):
     assert_gate(y.cpu().numpy().astype(np.float64)[:, rows], yr, A)
 
 
+
+def test_bench_model_attention_launches_full_size(w):
+    """The 62-layer decoder's attention launches as the benchmark runs them: w4a8_forward_multi
+    over four 5120 x 5120 layers (one launch) and w4a8_forward over a fifth, fp32 activations
+    of one token.  The five layers come from one oracle quantisation, rows permuted (r -> p r
+    mod N for odd p prime to 5) and row scales multiplied by g + 1, so each layer is distinct
+    and a launch that mixed them up would fail.  x_q and s_x bit-exact; 1024 sampled rows of
+    each layer within the bound."""
+    (N, K) = S.ATTN_SQUARE
+    say(f"bench launch: forward_multi 4 x {N}x{K} and forward {N}x{K}, M=1, fp32 x")
+    _, q0 = oracle_layer(N, K, 0)
+    qs = []
+    for g, p in enumerate((1, 3, 7, 11, 13)):
+        perm = (np.arange(N) * p) % N
+        qs.append(dict(packed=q0["packed"][perm], s_rel=q0["s_rel"][perm],
+                       s_ch=(q0["s_ch"][perm] * np.float32(g + 1)).astype(np.float32), cb=q0["cb"]))
+    for qset, seed in ((qs[:4], 3), (qs[4:], 4)):
+        x = S.activations(1, K, seed=seed)
+        xq_ref, sx_ref = O.prepare(x)
+        Ls = [gpu_layer(w, q) for q in qset]
+        x_q = torch.empty((1, K), dtype=torch.int8, device=DEV)
+        s_x = torch.empty((1,), dtype=torch.float32, device=DEV)
+        if len(Ls) > 1:
+            ys = w.forward_multi(gpu(x), Ls, x_q=x_q, s_x=s_x)
+        else:
+            ys = [w.forward(gpu(x), Ls[0], x_q=x_q, s_x=s_x)]
+        torch.cuda.synchronize()
+        assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+        assert np.array_equal(x_q.cpu().numpy(), xq_ref)
+        for g, q in enumerate(qset):
+            rows = sample(N, 1024, 200 + g)
+            yr, A = O.linear_ref(xq_ref, sx_ref, q["packed"], q["s_rel"], q["s_ch"], q["cb"], rows, None)
+            assert_gate(ys[g].cpu().numpy().astype(np.float64)[:, rows], yr, A)
+
+
 # ----------------------------------------------------------------------------- binding checks
 
 def test_binding_refuses_wrong_buffers(w):
